@@ -135,14 +135,28 @@ class Scheduler:
         computed = len(prefix_blocks) * self.block_size
         if computed >= num_prompt_tokens:
             raise ValueError("prefix must leave at least one token to compute")
+        if cdiv(num_prompt_tokens, self.block_size) > self.max_blocks:
+            raise ValueError("prompt longer than a block-table row can map")
         self.pool.share(prefix_blocks)
         self.reqs.append(Request(req_id, num_prompt_tokens, computed, prefix_blocks, False))
+
+    def add_partial(self, req_id: int, num_prompt_tokens: int, num_computed_tokens: int):
+        """A prompt whose first ``num_computed_tokens`` are already cached in
+        blocks it owns (taken from the pool now); prefill resumes there."""
+        if num_computed_tokens < 0 or num_prompt_tokens <= num_computed_tokens:
+            raise ValueError("need 0 <= computed < prompt")
+        if cdiv(num_prompt_tokens, self.block_size) > self.max_blocks:
+            raise ValueError("prompt longer than a block-table row can map")
+        blocks = self.pool.allocate(cdiv(num_computed_tokens, self.block_size))
+        self.reqs.append(Request(req_id, num_prompt_tokens, num_computed_tokens, blocks, False))
 
     def add_decode(self, req_id: int, context_len: int):
         """A running sequence with ``context_len`` tokens cached and one token to
         decode; its cache blocks are taken from the pool now."""
         if context_len <= 0:
             raise ValueError("empty context")
+        if cdiv(context_len + 1, self.block_size) > self.max_blocks:
+            raise ValueError("context longer than a block-table row can map")
         blocks = self.pool.allocate(cdiv(context_len, self.block_size))
         self.reqs.append(Request(req_id, context_len + 1, context_len, blocks, True))
 

@@ -1,0 +1,941 @@
+// Device side of libchunked_prefill_attn: the paged-cache write, the
+// segmented attention over a paged KV cache, and the log-sum-exp merge of
+// split rows, written for MI355X (gfx950, CDNA4), plus the C entry points
+// that validate host-visible arguments and launch them.
+//
+// Method (all citations are to the pages this library implements):
+//   * a chunk of active tokens first writes its K/V into the paged cache
+//     ("Prefill Processing", section "How Segmentation Works with KV
+//     Segments"), then attends to its sequence's cached KV, visited in
+//     kv_segment_size segments with the last one partial ("Prefill
+//     Processing", sections "Kernel Interface", "Partial KV Segment
+//     Handling"), and causally to itself ("Prefill Optimisation: Prefix
+//     Caching, Chunked Prefill, and Disaggregation", section 2, "Causal
+//     equivalence");
+//   * partial softmax states are rescaled and merged (same page, section 2:
+//     online softmax rescales running normalisers across blocks).
+//
+// Kernel design (gfx950):
+//   * A work item is 128 query rows = (token, query head) pairs of one KV
+//     head group, so one K/V tile in LDS serves all H/G heads of the group.
+//     4 waves x 32 rows; each wave owns 32 rows.
+//   * Scores are computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16_bf16 (fp32: v_mfma_f32_32x32x2_f32): a lane then
+//     holds 16 keys of one query row per 32-key block, so the row max and
+//     row sum are in-lane reductions plus one exchange with the lane 32 away.
+//   * The K rows fed to the A operand are permuted (bits 2 and 3 of the row
+//     index swapped) so that each lane's probabilities for one PV k-step are
+//     8 consecutive keys; with V stored transposed in the cache
+//     ([block, head, D, block_size]) the PV A operand is then a plain 16-byte
+//     LDS read.  O^T = V^T P^T accumulates in 4 (D=128) 32x32 fp32 tiles.
+//   * K and V^T tiles of 64 keys are gathered through the block table with
+//     16-byte loads into registers, double-buffered in LDS (XOR-swizzled
+//     16-byte chunks against bank conflicts), one barrier per tile.
+//   * Masking is a select to -inf before exp2; keys at or past the
+//     sequence's end are never loaded (zero-filled), so stale or NaN slots
+//     cannot reach the MFMA.
+//   * Workgroup ids are remapped so that each of the 8 XCDs runs a
+//     contiguous range of (KV head, item) pairs: one KV head per XCD L2 when
+//     G = 8.  Items are ordered longest-first within a sequence.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "chunked_prefill_attn.h"
+#include "cpa_plan.h"
+
+namespace cpa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kKeys = 64;   // keys per LDS tile
+constexpr int kXcds = 8;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <typename T> struct Elem;
+template <> struct Elem<__bf16> {
+    static constexpr int kPerChunk = 8;  // elements per 16-byte chunk
+    static constexpr int kPerFrag = 8;   // MFMA k elements per lane
+    typedef bf16x8 Frag;
+    __device__ static inline f32x16 mma(Frag a, Frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Elem<float> {
+    static constexpr int kPerChunk = 4;
+    static constexpr int kPerFrag = 1;
+    typedef float Frag;
+    __device__ static inline f32x16 mma(Frag a, Frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+};
+
+__device__ __forceinline__ int swap_bits23(int x) {
+    return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// Physical workgroup ids go round-robin over the XCDs; give XCD x the
+// contiguous logical range [start_x, start_x + count_x).
+__device__ __forceinline__ int xcd_remap(int pid, int n) {
+    const int q = n / kXcds, r = n % kXcds;
+    const int x = pid % kXcds, k = pid / kXcds;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
+}
+
+// Zero the elements of a 16-byte chunk from index `keep` on.
+template <typename T>
+__device__ __forceinline__ u32x4 keep_first(u32x4 v, int keep) {
+    constexpr int kPerWord = 4 / sizeof(T);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t mask = 0;
+#pragma unroll
+        for (int e = 0; e < kPerWord; ++e) {
+            if (w * kPerWord + e < keep) mask |= (sizeof(T) == 2 ? 0xffffu : 0xffffffffu) << (16 * e);
+        }
+        v[w] &= mask;
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Attention kernel
+// ---------------------------------------------------------------------------
+struct AttnParams {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    void* out;
+    float* lse;
+    const int32_t* cu;
+    const int32_t* cached;
+    const int32_t* block_table;
+    const int4* seq_info;
+    const int4* items;
+    float2* part_ml;
+    float* part_o;
+    int32_t num_items;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t hpg;
+    int32_t block_size;
+    int32_t log2_bs;
+    int32_t max_blocks;
+    int32_t num_blocks;
+    int32_t total_q;
+    int32_t dec_thresh;
+    int32_t split_pre;
+    int32_t split_dec;
+    float scale_log2;   // softmax scale * log2(e)
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
+    using E = Elem<T>;
+    using Frag = typename E::Frag;
+    constexpr int EPC = E::kPerChunk;
+    constexpr int KPL = E::kPerFrag;
+    constexpr int NCK = D / EPC;                    // 16-B chunks per K row
+    constexpr int NCV = kKeys / EPC;                // 16-B chunks per V^T row
+    constexpr int SWK = (NCK < 16 ? NCK : 16) - 1;  // K swizzle mask
+    constexpr int SWV = 7;                          // V^T swizzle mask
+    constexpr int NLD = kKeys * NCK / kThreads;     // 16-B loads per thread per tile (each of K, V)
+    constexpr int NQF = D / (2 * KPL);              // Q fragments (k-steps over D)
+    constexpr int NKS = kKeys / (2 * KPL);          // PV k-steps per tile
+    constexpr int NDT = D / 32;                     // 32-row tiles of O^T
+    constexpr int QCH = (D / 2) / EPC;              // 16-B chunks in a lane's half row of Q
+    static_assert(NLD * kThreads == kKeys * NCK, "tile must split evenly over threads");
+
+    __shared__ __attribute__((aligned(16))) T lds_k[2][kKeys * D];
+    __shared__ __attribute__((aligned(16))) T lds_v[2][D * kKeys];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int half = lane >> 5;
+    const int lrow = lane & 31;
+    const int G = p.num_kv_heads;
+
+    const int logical = xcd_remap(blockIdx.x, p.num_items * G);
+    const int g = logical / p.num_items;
+    const int4 item = p.items[logical - g * p.num_items];
+    const int b = item.x, rt = item.y, split = item.z, nsplit = item.w;
+
+    const int q0 = p.cu[b];
+    const int n = p.cu[b + 1] - q0;
+    const int c = p.cached[b];
+    const int kv_len = c + n;
+    const int hpg = p.hpg;
+    const int rows_total = n * hpg;
+    const int row0 = rt * kRows;
+    const int t_last = (min(row0 + kRows, rows_total) - 1) / hpg;
+    const int P = keys_per_item(n, p.dec_thresh, p.split_pre, p.split_dec);
+    const int k0 = (nsplit == 1) ? 0 : split * P;
+    const int k1 = (nsplit == 1) ? kv_len : min(k0 + P, kv_len);
+    const int kend = min(k1, c + t_last + 1);
+
+    // this lane's query row
+    const int R = row0 + wave * 32 + lrow;
+    const bool row_ok = R < rows_total;
+    const int t = row_ok ? R / hpg : 0;
+    const int head = g * hpg + (row_ok ? R - (R / hpg) * hpg : 0);
+    const int lim = row_ok ? c + t : -1;          // last key position the row may see
+    const int wrow0 = row0 + wave * 32;
+    const bool wave_on = wrow0 < rows_total;
+    const int wt_min = wrow0 / hpg;
+    const int wt_max = (min(wrow0 + 32, rows_total) - 1) / hpg;
+
+    const int32_t* bt = p.block_table + (size_t)b * p.max_blocks;
+    const T* kc = (const T*)p.k_cache;
+    const T* vc = (const T*)p.v_cache;
+    const int bs = p.block_size;
+    const int lbs = p.log2_bs;
+
+    // Q: lane holds elements [half*D/2, half*D/2 + D/2) of its row
+    u32x4 qc[QCH];
+    {
+        const T* qp = (const T*)p.q + ((size_t)(q0 + t) * p.num_heads + head) * D + half * (D / 2);
+#pragma unroll
+        for (int i = 0; i < QCH; ++i)
+            qc[i] = row_ok ? *(const u32x4*)(qp + i * EPC) : u32x4{0u, 0u, 0u, 0u};
+    }
+    auto qfrag = [&](int f) -> Frag {
+        if constexpr (KPL == 8) {
+            return __builtin_bit_cast(Frag, qc[f]);
+        } else {
+            return __builtin_bit_cast(float, qc[f / 4][f % 4]);
+        }
+    };
+
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x16 oacc[NDT];
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) oacc[i] = f32x16{};
+
+    u32x4 kreg[NLD], vreg[NLD];
+    auto load_tile = [&](int ts) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int cidx = i * kThreads + tid;
+            const int key = cidx / NCK, ch = cidx % NCK;
+            const int j = ts + key;
+            u32x4 val = {0u, 0u, 0u, 0u};
+            if (j < kv_len) {
+                const int blk = bt[j >> lbs];
+                if ((unsigned)blk < (unsigned)p.num_blocks)
+                    val = *(const u32x4*)(kc + (((size_t)blk * G + g) * bs + (j & (bs - 1))) * D +
+                                          ch * EPC);
+            }
+            kreg[i] = val;
+        }
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int cidx = i * kThreads + tid;
+            const int d = cidx / NCV, kcn = cidx % NCV;
+            const int j = ts + kcn * EPC;
+            u32x4 val = {0u, 0u, 0u, 0u};
+            if (j < kv_len) {
+                const int blk = bt[j >> lbs];
+                if ((unsigned)blk < (unsigned)p.num_blocks) {
+                    val = *(const u32x4*)(vc + (((size_t)blk * G + g) * D + d) * bs + (j & (bs - 1)));
+                    if (kv_len - j < EPC) val = keep_first<T>(val, kv_len - j);
+                }
+            }
+            vreg[i] = val;
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int cidx = i * kThreads + tid;
+            const int key = cidx / NCK, ch = cidx % NCK;
+            const int sw = swap_bits23(key & 31) & SWK;
+            *(u32x4*)&lds_k[buf][key * D + (ch ^ sw) * EPC] = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int cidx = i * kThreads + tid;
+            const int d = cidx / NCV, kcn = cidx % NCV;
+            const int sw = ((d & 7) ^ ((d >> 3) & 1)) & SWV;
+            *(u32x4*)&lds_v[buf][d * kKeys + (kcn ^ sw) * EPC] = vreg[i];
+        }
+    };
+
+    auto compute = [&](int buf, int ts) {
+        // S^T = K Q^T for two 32-key blocks
+        f32x16 sacc[2];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            sacc[sub] = f32x16{};
+            const T* kb = &lds_k[buf][(sub * 32 + swap_bits23(lrow)) * D];
+            const int sw = lane & SWK;
+#pragma unroll
+            for (int f = 0; f < NQF; ++f) {
+                const int e = half * (D / 2) + f * KPL;
+                const int ch = e / EPC, within = e % EPC;
+                const Frag a = *(const Frag*)(kb + (ch ^ sw) * EPC + within);
+                sacc[sub] = E::mma(a, qfrag(f), sacc[sub]);
+            }
+        }
+        // register r of block sub holds key ts + sub*32 + 16*(r/8) + 8*half + r%8
+        const bool need_mask = (ts + kKeys - 1 > c + wt_min) || (ts + kKeys > k1);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = sacc[sub][r] * p.scale_log2;
+                if (need_mask) {
+                    const int j = ts + sub * 32 + ((r >> 3) << 4) + (half << 3) + (r & 7);
+                    if (j > lim || j >= k1) x = -INFINITY;
+                }
+                sacc[sub][r] = x;
+                mx = fmaxf(mx, x);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        float rs = 0.f;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pv = __builtin_amdgcn_exp2f(sacc[sub][r] - m_use);
+                sacc[sub][r] = pv;
+                rs += pv;
+            }
+        }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
+
+        // P^T fragments for the PV k-steps
+        Frag pf[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            if constexpr (KPL == 8) {
+                const int sub = ks >> 1, r0 = (ks & 1) * 8;
+                bf16x8 v;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = (__bf16)sacc[sub][r0 + i];
+                pf[ks] = v;
+            } else {
+                pf[ks] = sacc[ks >> 4][ks & 15];
+            }
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int drow = dt * 32 + lrow;
+            const T* vb = &lds_v[buf][drow * kKeys];
+            const int sw = ((drow & 7) ^ ((drow >> 3) & 1)) & SWV;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                int key0;
+                if constexpr (KPL == 8) {
+                    key0 = ks * 16 + half * 8;
+                } else {
+                    const int sub = ks >> 4, r = ks & 15;
+                    key0 = sub * 32 + ((r >> 3) << 4) + (half << 3) + (r & 7);
+                }
+                const int ch = key0 / EPC, within = key0 % EPC;
+                const Frag a = *(const Frag*)(vb + (ch ^ sw) * EPC + within);
+                oacc[dt] = E::mma(a, pf[ks], oacc[dt]);
+            }
+        }
+    };
+
+    if (kend > k0) {
+        const int tile0 = k0 / kKeys;
+        const int ntiles = (kend - k0 + kKeys - 1) / kKeys;
+        load_tile(tile0 * kKeys);
+        store_tile(0);
+        for (int it = 0; it < ntiles; ++it) {
+            const int ts = (tile0 + it) * kKeys;
+            if (it + 1 < ntiles) load_tile(ts + kKeys);
+            __syncthreads();
+            if (wave_on && ts <= c + wt_max) compute(it & 1, ts);
+            if (it + 1 < ntiles) store_tile((it + 1) & 1);
+        }
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (!row_ok) return;
+    if (nsplit == 1) {
+        const float inv = 1.f / l_tot;
+        T* op = (T*)p.out + ((size_t)(q0 + t) * p.num_heads + head) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int d = dt * 32 + rq * 8 + half * 4;
+                if constexpr (sizeof(T) == 2) {
+                    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                    bf16x4 v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = (__bf16)(oacc[dt][rq * 4 + i] * inv);
+                    *(bf16x4*)(op + d) = v;
+                } else {
+                    f32x4 v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = oacc[dt][rq * 4 + i] * inv;
+                    *(f32x4*)(op + d) = v;
+                }
+            }
+        }
+        if (p.lse && half == 0)
+            p.lse[(size_t)head * p.total_q + q0 + t] = (m_run + __log2f(l_tot)) * kLn2;
+    } else {
+        const size_t pidx = (size_t)p.seq_info[b].z + ((size_t)split * n + t) * p.num_heads + head;
+        float* po = p.part_o + pidx * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int d = dt * 32 + rq * 8 + half * 4;
+                f32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = oacc[dt][rq * 4 + i];
+                *(f32x4*)(po + d) = v;
+            }
+        }
+        if (half == 0) p.part_ml[pidx] = make_float2(m_run, l_tot);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of split rows: m = max m_s, l = sum l_s 2^(m_s - m),
+// O = sum O~_s 2^(m_s - m) / l  (states kept in log2 units).
+// ---------------------------------------------------------------------------
+struct MergeParams {
+    const int32_t* cu;
+    const int4* seq_info;
+    const int2* merge;
+    const float2* part_ml;
+    const float* part_o;
+    void* out;
+    float* lse;
+    int32_t num_heads;
+    int32_t total_q;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
+    const int2 e = p.merge[blockIdx.x];
+    const int b = e.x, t = e.y;
+    const int q0 = p.cu[b];
+    const int n = p.cu[b + 1] - q0;
+    const int4 si = p.seq_info[b];
+    const int nsplit = si.y;
+    const size_t base = (size_t)si.z;
+    const int H = p.num_heads;
+    constexpr int NC = D / 4;
+    for (int idx = threadIdx.x; idx < H * NC; idx += kThreads) {
+        const int h = idx / NC, dc = idx % NC;
+        float m = -INFINITY;
+        for (int s = 0; s < nsplit; ++s)
+            m = fmaxf(m, p.part_ml[base + ((size_t)s * n + t) * H + h].x);
+        float l = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < nsplit; ++s) {
+            const size_t pi = base + ((size_t)s * n + t) * H + h;
+            const float2 ml = p.part_ml[pi];
+            if (ml.x == -INFINITY) continue;
+            const float w = __builtin_amdgcn_exp2f(ml.x - m);
+            l += w * ml.y;
+            acc += w * *(const f32x4*)(p.part_o + pi * D + dc * 4);
+        }
+        const float inv = 1.f / l;
+        T* op = (T*)p.out + ((size_t)(q0 + t) * H + h) * D + dc * 4;
+        if constexpr (sizeof(T) == 2) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[i] * inv);
+            *(bf16x4*)op = v;
+        } else {
+            *(f32x4*)op = acc * inv;
+        }
+        if (p.lse && dc == 0) p.lse[(size_t)h * p.total_q + q0 + t] = (m + __log2f(l)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prep kernel: cache write (all but the last workgroup) and the work plan
+// (last workgroup).
+// ---------------------------------------------------------------------------
+struct PrepParams {
+    const void* k_new;
+    const void* v_new;
+    void* k_cache;
+    void* v_cache;
+    const int64_t* slots;
+    int32_t total_q;
+    int32_t num_kv_heads;
+    int32_t block_size;
+    int32_t log2_bs;
+    int32_t num_blocks;
+    int32_t cache_wgs;
+    // plan (only when plan != 0)
+    int32_t plan;
+    const int32_t* cu;
+    const int32_t* cached;
+    int32_t num_seqs;
+    int32_t hpg;
+    int32_t num_heads;
+    int32_t dec_thresh;
+    int32_t split_pre;
+    int32_t split_dec;
+    int4* seq_info;
+    int4* items;
+    int2* merge;
+    int32_t* header;
+};
+
+constexpr int kPrepSmem = 2 * (kMaxSeqs + 1) * 4 > 64 * (128 + 1) * 4 ? 2 * (kMaxSeqs + 1) * 4
+                                                                        : 64 * (128 + 1) * 4;
+
+// Rows of 64 new tokens of KV head g go to their slots.  K rows are copied
+// with 16-byte stores; V is staged in LDS and written as columns of the
+// transposed layout, lanes over tokens so that neighbouring slots coalesce.
+template <typename T, int D>
+__device__ void cache_write(const PrepParams& p, char* smem) {
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr int NCK = D / EPC;
+    constexpr int LD = D + 4 / (int)sizeof(T);   // LDS pitch: one extra 32-bit word
+    T* tile = (T*)smem;
+    const int G = p.num_kv_heads;
+    const int grp = blockIdx.x / G, g = blockIdx.x - grp * G;
+    const int tok0 = grp * 64;
+    const int ntok = min(64, p.total_q - tok0);
+    const int tid = threadIdx.x;
+    const T* kn = (const T*)p.k_new;
+    const T* vn = (const T*)p.v_new;
+    T* kc = (T*)p.k_cache;
+    T* vc = (T*)p.v_cache;
+    const int bs = p.block_size;
+    const int64_t nslots = (int64_t)p.num_blocks * bs;
+    for (int cidx = tid; cidx < ntok * NCK; cidx += kThreads) {
+        const int tk = cidx / NCK, ch = cidx - (cidx / NCK) * NCK;
+        const size_t src = ((size_t)(tok0 + tk) * G + g) * D + ch * EPC;
+        const u32x4 kv = *(const u32x4*)(kn + src);
+        const u32x4 vv = *(const u32x4*)(vn + src);
+        uint32_t* dst = (uint32_t*)(tile + tk * LD + ch * EPC);
+        dst[0] = vv.x;
+        dst[1] = vv.y;
+        dst[2] = vv.z;
+        dst[3] = vv.w;
+        const int64_t slot = p.slots[tok0 + tk];
+        if (slot >= 0 && slot < nslots) {
+            const int64_t blk = slot >> p.log2_bs;
+            const int off = (int)(slot & (bs - 1));
+            *(u32x4*)(kc + ((blk * G + g) * bs + off) * D + ch * EPC) = kv;
+        }
+    }
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    if (lane < ntok) {
+        const int64_t slot = p.slots[tok0 + lane];
+        if (slot >= 0 && slot < nslots) {
+            const int64_t blk = slot >> p.log2_bs;
+            const int off = (int)(slot & (bs - 1));
+            T* col = vc + (blk * G + g) * D * (int64_t)bs + off;
+            for (int d = wave; d < D; d += 4) col[(size_t)d * bs] = tile[lane * LD + d];
+        }
+    }
+}
+
+__device__ void build_plan(const PrepParams& p, char* smem) {
+    int* s_item = (int*)smem;                 // [kMaxSeqs + 1]
+    int* s_merge = s_item + (kMaxSeqs + 1);   // [kMaxSeqs + 1]
+    __shared__ long long sc_items[kThreads];
+    __shared__ long long sc_parts[kThreads];
+    __shared__ int sc_merge[kThreads];
+    const int B = p.num_seqs, tid = threadIdx.x;
+    const int per = (B + kThreads - 1) / kThreads;
+    const int b_lo = min(B, tid * per), b_hi = min(B, b_lo + per);
+    long long items = 0, parts = 0;
+    int merge = 0;
+    for (int b = b_lo; b < b_hi; ++b) {
+        const int n = p.cu[b + 1] - p.cu[b];
+        const SeqPlan sp = seq_plan(n, p.cached[b], p.hpg, p.num_heads, p.dec_thresh, p.split_pre,
+                                    p.split_dec);
+        items += sp.items;
+        parts += sp.parts;
+        merge += sp.merge;
+    }
+    sc_items[tid] = items;
+    sc_parts[tid] = parts;
+    sc_merge[tid] = merge;
+    __syncthreads();
+    if (tid == 0) {   // exclusive scan over the 256 thread sums
+        long long ai = 0, ap = 0;
+        int am = 0;
+        for (int i = 0; i < kThreads; ++i) {
+            const long long xi = sc_items[i], xp = sc_parts[i];
+            const int xm = sc_merge[i];
+            sc_items[i] = ai;
+            sc_parts[i] = ap;
+            sc_merge[i] = am;
+            ai += xi;
+            ap += xp;
+            am += xm;
+        }
+        s_item[B] = (int)ai;
+        s_merge[B] = am;
+        p.header[0] = (int)ai;
+        p.header[1] = am;
+        p.header[2] = (int)ap;
+    }
+    __syncthreads();
+    long long io = sc_items[tid], po = sc_parts[tid];
+    int mo = sc_merge[tid];
+    for (int b = b_lo; b < b_hi; ++b) {
+        const int n = p.cu[b + 1] - p.cu[b];
+        const SeqPlan sp = seq_plan(n, p.cached[b], p.hpg, p.num_heads, p.dec_thresh, p.split_pre,
+                                    p.split_dec);
+        p.seq_info[b] = make_int4((int)io, sp.nsplit, (int)po, mo);
+        s_item[b] = (int)io;
+        s_merge[b] = mo;
+        io += sp.items;
+        po += sp.parts;
+        mo += sp.merge;
+    }
+    __syncthreads();
+    const int total_items = s_item[B];
+    for (int i = tid; i < total_items; i += kThreads) {
+        int lo = 0, hi = B;   // s_item[lo] <= i < s_item[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_item[mid] <= i) lo = mid; else hi = mid;
+        }
+        const int n = p.cu[lo + 1] - p.cu[lo];
+        const SeqPlan sp = seq_plan(n, p.cached[lo], p.hpg, p.num_heads, p.dec_thresh, p.split_pre,
+                                    p.split_dec);
+        const int local = i - s_item[lo];
+        const int rt = sp.tiles - 1 - local / sp.nsplit;   // longest row tiles first
+        p.items[i] = make_int4(lo, rt, local % sp.nsplit, sp.nsplit);
+    }
+    const int total_merge = s_merge[B];
+    for (int i = tid; i < total_merge; i += kThreads) {
+        int lo = 0, hi = B;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_merge[mid] <= i) lo = mid; else hi = mid;
+        }
+        p.merge[i] = make_int2(lo, i - s_merge[lo]);
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void prep_kernel(const PrepParams p) {
+    __shared__ __attribute__((aligned(16))) char smem[kPrepSmem];
+    if ((int)blockIdx.x >= p.cache_wgs) {
+        build_plan(p, smem);
+        return;
+    }
+    cache_write<T, D>(p, smem);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+struct Resolved {
+    int32_t hpg, dec_thresh, split_pre, split_dec, log2_bs, seg;
+    int64_t items, parts;
+    int64_t merge;
+    WsLayout ws;
+};
+
+inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+inline int ilog2(int x) {
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
+}
+
+cpa_status check_common(const cpa_attn_args* a) {
+    if (!a) return CPA_ERR_INVALID_ARG;
+    if (a->dtype != CPA_BF16 && a->dtype != CPA_FP32) return CPA_ERR_INVALID_ARG;
+    if (a->num_kv_heads <= 0 || a->total_q < 0) return CPA_ERR_INVALID_ARG;
+    if (a->head_dim <= 0 || a->block_size <= 0 || a->num_blocks <= 0) return CPA_ERR_INVALID_ARG;
+    if (a->head_dim != 64 && a->head_dim != 128) return CPA_ERR_UNSUPPORTED;
+    if (!is_pow2(a->block_size) || a->block_size < 8 || a->block_size > 512) return CPA_ERR_UNSUPPORTED;
+    if ((int64_t)a->num_blocks * a->block_size > (int64_t)1 << 40) return CPA_ERR_INVALID_ARG;
+    return CPA_OK;
+}
+
+cpa_status resolve(const cpa_attn_args* a, Resolved* r) {
+    cpa_status st = check_common(a);
+    if (st != CPA_OK) return st;
+    if (a->num_seqs <= 0 || a->num_heads <= 0 || a->max_blocks_per_seq <= 0) return CPA_ERR_INVALID_ARG;
+    if (a->num_seqs > kMaxSeqs) return CPA_ERR_UNSUPPORTED;
+    if (a->num_heads % a->num_kv_heads != 0) return CPA_ERR_INVALID_ARG;
+    if (!std::isfinite(a->scale)) return CPA_ERR_INVALID_ARG;
+    const int S = a->kv_segment_size;
+    if (S != 0 && S != 512 && S != 1024 && S != 2048 && S != 4096) return CPA_ERR_INVALID_ARG;
+    if (S != 0 && S % a->block_size != 0) return CPA_ERR_INVALID_ARG;
+    if (a->decode_token_threshold < 0) return CPA_ERR_INVALID_ARG;
+    const int seg = S ? S : 1024;
+    auto resolve_split = [&](int32_t v, int32_t auto_value, int32_t* outv) -> cpa_status {
+        if (v == 0) *outv = auto_value;
+        else if (v < 0) *outv = kNoSplit;
+        else if (v % seg != 0) return CPA_ERR_INVALID_ARG;
+        else *outv = v;
+        return CPA_OK;
+    };
+    r->seg = seg;
+    r->hpg = a->num_heads / a->num_kv_heads;
+    r->dec_thresh = a->decode_token_threshold ? a->decode_token_threshold : 1;
+    r->log2_bs = ilog2(a->block_size);
+    if ((st = resolve_split(a->split_keys_prefill, kNoSplit, &r->split_pre)) != CPA_OK) return st;
+    if ((st = resolve_split(a->split_keys_decode, seg, &r->split_dec)) != CPA_OK) return st;
+    if (!a->h_cu_seqlens_q || !a->h_cached_seq_len) return CPA_ERR_INVALID_ARG;
+    const int32_t* cu = a->h_cu_seqlens_q;
+    const int32_t* cc = a->h_cached_seq_len;
+    if (cu[0] != 0 || cu[a->num_seqs] != a->total_q) return CPA_ERR_INVALID_ARG;
+    int64_t items = 0, parts = 0, merge = 0;
+    for (int b = 0; b < a->num_seqs; ++b) {
+        const int64_t n = (int64_t)cu[b + 1] - cu[b];
+        if (n < 0 || cc[b] < 0) return CPA_ERR_INVALID_ARG;
+        if (S == 0 && cc[b] != 0) return CPA_ERR_INVALID_ARG;
+        const int64_t kv = cc[b] + n;
+        if (kv >= ((int64_t)1 << 30)) return CPA_ERR_INVALID_ARG;
+        if ((kv + a->block_size - 1) / a->block_size > a->max_blocks_per_seq) return CPA_ERR_INVALID_ARG;
+        const SeqPlan sp = seq_plan((int32_t)n, cc[b], r->hpg, a->num_heads, r->dec_thresh, r->split_pre,
+                                    r->split_dec);
+        items += sp.items;
+        parts += sp.parts;
+        merge += sp.merge;
+    }
+    if (items * a->num_kv_heads >= ((int64_t)1 << 31) || parts >= ((int64_t)1 << 31)) return CPA_ERR_UNSUPPORTED;
+    r->items = items;
+    r->parts = parts;
+    r->merge = merge;
+    r->ws = ws_layout(a->num_seqs, items, merge, parts, a->head_dim);
+    return CPA_OK;
+}
+
+cpa_status check_pointers(const cpa_attn_args* a, bool attention) {
+    if (a->total_q > 0 && (!a->k_new || !a->v_new || !a->slot_mapping)) return CPA_ERR_INVALID_ARG;
+    if (!a->k_cache || !a->v_cache) return CPA_ERR_INVALID_ARG;
+    if (attention) {
+        if (a->total_q > 0 && (!a->q || !a->out)) return CPA_ERR_INVALID_ARG;
+        if (!a->cu_seqlens_q || !a->cached_seq_len || !a->block_table) return CPA_ERR_INVALID_ARG;
+    }
+    return CPA_OK;
+}
+
+template <typename T, int D>
+cpa_status launch_prep(const cpa_attn_args* a, const Resolved* r, bool plan, hipStream_t stream) {
+    PrepParams p{};
+    p.k_new = a->k_new;
+    p.v_new = a->v_new;
+    p.k_cache = a->k_cache;
+    p.v_cache = a->v_cache;
+    p.slots = a->slot_mapping;
+    p.total_q = a->total_q;
+    p.num_kv_heads = a->num_kv_heads;
+    p.block_size = a->block_size;
+    p.log2_bs = ilog2(a->block_size);
+    p.num_blocks = a->num_blocks;
+    p.cache_wgs = ((a->total_q + 63) / 64) * a->num_kv_heads;
+    p.plan = plan ? 1 : 0;
+    if (plan) {
+        char* ws = (char*)a->workspace;
+        p.cu = a->cu_seqlens_q;
+        p.cached = a->cached_seq_len;
+        p.num_seqs = a->num_seqs;
+        p.hpg = r->hpg;
+        p.num_heads = a->num_heads;
+        p.dec_thresh = r->dec_thresh;
+        p.split_pre = r->split_pre;
+        p.split_dec = r->split_dec;
+        p.header = (int32_t*)ws;
+        p.seq_info = (int4*)(ws + r->ws.seq_info);
+        p.items = (int4*)(ws + r->ws.items);
+        p.merge = (int2*)(ws + r->ws.merge);
+    }
+    const int grid = p.cache_wgs + (plan ? 1 : 0);
+    if (grid == 0) return CPA_OK;
+    hipLaunchKernelGGL((prep_kernel<T, D>), dim3(grid), dim3(kThreads), 0, stream, p);
+    return hipGetLastError() == hipSuccess ? CPA_OK : CPA_ERR_HIP;
+}
+
+template <typename T, int D>
+cpa_status launch_attention(const cpa_attn_args* a, const Resolved* r, hipStream_t stream) {
+    char* ws = (char*)a->workspace;
+    if (r->items > 0) {
+        AttnParams p{};
+        p.q = a->q;
+        p.k_cache = a->k_cache;
+        p.v_cache = a->v_cache;
+        p.out = a->out;
+        p.lse = a->lse;
+        p.cu = a->cu_seqlens_q;
+        p.cached = a->cached_seq_len;
+        p.block_table = a->block_table;
+        p.seq_info = (const int4*)(ws + r->ws.seq_info);
+        p.items = (const int4*)(ws + r->ws.items);
+        p.part_ml = (float2*)(ws + r->ws.part_ml);
+        p.part_o = (float*)(ws + r->ws.part_o);
+        p.num_items = (int32_t)r->items;
+        p.num_heads = a->num_heads;
+        p.num_kv_heads = a->num_kv_heads;
+        p.hpg = r->hpg;
+        p.block_size = a->block_size;
+        p.log2_bs = r->log2_bs;
+        p.max_blocks = a->max_blocks_per_seq;
+        p.num_blocks = a->num_blocks;
+        p.total_q = a->total_q;
+        p.dec_thresh = r->dec_thresh;
+        p.split_pre = r->split_pre;
+        p.split_dec = r->split_dec;
+        p.scale_log2 = a->scale * 1.44269504088896340736f;
+        const int grid = (int)(r->items * a->num_kv_heads);
+        hipLaunchKernelGGL((attn_kernel<T, D>), dim3(grid), dim3(kThreads), 0, stream, p);
+        if (hipGetLastError() != hipSuccess) return CPA_ERR_HIP;
+    }
+    if (r->merge > 0) {
+        MergeParams m{};
+        m.cu = a->cu_seqlens_q;
+        m.seq_info = (const int4*)(ws + r->ws.seq_info);
+        m.merge = (const int2*)(ws + r->ws.merge);
+        m.part_ml = (const float2*)(ws + r->ws.part_ml);
+        m.part_o = (const float*)(ws + r->ws.part_o);
+        m.out = a->out;
+        m.lse = a->lse;
+        m.num_heads = a->num_heads;
+        m.total_q = a->total_q;
+        hipLaunchKernelGGL((merge_kernel<T, D>), dim3((int)r->merge), dim3(kThreads), 0, stream, m);
+        if (hipGetLastError() != hipSuccess) return CPA_ERR_HIP;
+    }
+    return CPA_OK;
+}
+
+}  // namespace cpa
+
+using namespace cpa;
+
+namespace {
+
+template <typename T, int D>
+cpa_status run_prep(const cpa_attn_args* a, const Resolved* r, bool plan, hipStream_t s) {
+    return launch_prep<T, D>(a, r, plan, s);
+}
+
+cpa_status prep_dispatch(const cpa_attn_args* a, const Resolved* r, bool plan, hipStream_t s) {
+    if (a->dtype == CPA_BF16)
+        return a->head_dim == 128 ? run_prep<__bf16, 128>(a, r, plan, s) : run_prep<__bf16, 64>(a, r, plan, s);
+    return a->head_dim == 128 ? run_prep<float, 128>(a, r, plan, s) : run_prep<float, 64>(a, r, plan, s);
+}
+
+cpa_status attn_dispatch(const cpa_attn_args* a, const Resolved* r, hipStream_t s) {
+    if (a->dtype == CPA_BF16)
+        return a->head_dim == 128 ? launch_attention<__bf16, 128>(a, r, s)
+                                  : launch_attention<__bf16, 64>(a, r, s);
+    if (a->head_dim == 128) return CPA_ERR_UNSUPPORTED;   // fp32 D=128 needs 128 KiB of LDS tiles
+    return launch_attention<float, 64>(a, r, s);
+}
+
+cpa_status check_workspace(const cpa_attn_args* a, const Resolved* r) {
+    if (!a->workspace || a->workspace_bytes < r->ws.total) return CPA_ERR_WORKSPACE;
+    return CPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cpa_status_string(int status) {
+    switch (status) {
+        case CPA_OK: return "ok";
+        case CPA_ERR_INVALID_ARG: return "invalid argument";
+        case CPA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case CPA_ERR_BUDGET_EXHAUSTED: return "token budget exhausted";
+        case CPA_ERR_OUT_OF_BLOCKS: return "out of KV-cache blocks";
+        case CPA_ERR_HIP: return "HIP error";
+        case CPA_ERR_WORKSPACE: return "workspace missing or too small";
+        case CPA_ERR_NOT_FOUND: return "unknown request";
+        default: return "unknown status";
+    }
+}
+
+int cpa_abi_version(void) { return CPA_ABI_VERSION; }
+
+cpa_status cpa_check_args(const cpa_attn_args* a) {
+    Resolved r;
+    cpa_status st = resolve(a, &r);
+    if (st != CPA_OK) return st;
+    if (a->dtype == CPA_FP32 && a->head_dim == 128) return CPA_ERR_UNSUPPORTED;
+    return check_pointers(a, true);
+}
+
+cpa_status cpa_plan_counts(const cpa_attn_args* a, cpa_plan_info* info) {
+    if (!info) return CPA_ERR_INVALID_ARG;
+    Resolved r;
+    cpa_status st = resolve(a, &r);
+    if (st != CPA_OK) return st;
+    info->num_items = (int32_t)r.items;
+    info->num_merge_rows = (int32_t)r.merge;
+    info->num_partials = r.parts;
+    info->split_keys_prefill = r.split_pre == kNoSplit ? 0 : r.split_pre;
+    info->split_keys_decode = r.split_dec == kNoSplit ? 0 : r.split_dec;
+    info->workspace_bytes = r.ws.total;
+    return CPA_OK;
+}
+
+cpa_status cpa_workspace_bytes(const cpa_attn_args* a, size_t* bytes) {
+    if (!bytes) return CPA_ERR_INVALID_ARG;
+    Resolved r;
+    cpa_status st = resolve(a, &r);
+    if (st != CPA_OK) return st;
+    *bytes = r.ws.total;
+    return CPA_OK;
+}
+
+cpa_status cpa_reshape_and_cache(const cpa_attn_args* a, void* stream) {
+    cpa_status st = check_common(a);
+    if (st != CPA_OK) return st;
+    if ((st = check_pointers(a, false)) != CPA_OK) return st;
+    Resolved r{};
+    return prep_dispatch(a, &r, false, (hipStream_t)stream);
+}
+
+cpa_status cpa_prepare(const cpa_attn_args* a, void* stream) {
+    Resolved r;
+    cpa_status st = resolve(a, &r);
+    if (st != CPA_OK) return st;
+    if (a->dtype == CPA_FP32 && a->head_dim == 128) return CPA_ERR_UNSUPPORTED;
+    if ((st = check_pointers(a, true)) != CPA_OK) return st;
+    if ((st = check_workspace(a, &r)) != CPA_OK) return st;
+    return prep_dispatch(a, &r, true, (hipStream_t)stream);
+}
+
+cpa_status cpa_attention(const cpa_attn_args* a, void* stream) {
+    Resolved r;
+    cpa_status st = resolve(a, &r);
+    if (st != CPA_OK) return st;
+    if ((st = check_pointers(a, true)) != CPA_OK) return st;
+    if ((st = check_workspace(a, &r)) != CPA_OK) return st;
+    return attn_dispatch(a, &r, (hipStream_t)stream);
+}
+
+cpa_status cpa_chunked_prefill_attn(const cpa_attn_args* a, void* stream) {
+    cpa_status st = cpa_prepare(a, stream);
+    if (st != CPA_OK) return st;
+    return cpa_attention(a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports every function include/*.h declares, and
+refuses bad host-visible arguments before touching the device.  CPU only: no
+call here launches a kernel."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+from chunked_prefill_paged_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(cpa_[a-z0-9_]+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 20
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared but not exported"
+    assert set(declared) == set(_lib.SIGNATURES), "binding and header disagree"
+    assert lib.cpa_abi_version() == 1
+
+
+def test_status_strings():
+    for code in range(8):
+        assert _lib.status_string(code) != "unknown status"
+    assert _lib.status_string(99) == "unknown status"
+
+
+def _args(**over):
+    a = _lib.AttnArgs()
+    a.dtype, a.num_seqs, a.total_q, a.num_heads, a.num_kv_heads = 0, 2, 300, 32, 8
+    a.head_dim, a.block_size, a.kv_segment_size = 128, 16, 1024
+    a.max_blocks_per_seq, a.num_blocks, a.scale = 200, 1000, 128 ** -0.5
+    cu = np.array([0, 100, 300], dtype=np.int32)
+    cached = np.array([1000, 0], dtype=np.int32)
+    keep = [cu, cached]
+    for k, v in over.items():
+        if k == "cu":
+            cu = np.asarray(v, dtype=np.int32); keep.append(cu)
+        elif k == "cached":
+            cached = np.asarray(v, dtype=np.int32); keep.append(cached)
+        else:
+            setattr(a, k, v)
+    a.h_cu_seqlens_q, a.h_cached_seq_len = cu.ctypes.data, cached.ctypes.data
+    fake = 0x1000   # never dereferenced: only host checks run here
+    for f in ("q", "k_new", "v_new", "k_cache", "v_cache", "cu_seqlens_q", "cached_seq_len",
+              "block_table", "slot_mapping", "out"):
+        setattr(a, f, fake)
+    return a, keep
+
+
+def _plan(a):
+    info = _lib.PlanInfo()
+    st = _lib.lib().cpa_plan_counts(ctypes.byref(a), ctypes.byref(info))
+    return st, info
+
+
+def test_plan_counts_for_a_valid_batch():
+    a, _keep = _args()
+    st, info = _plan(a)
+    assert st == 0
+    # seq 0: 100 tokens x 4 heads = 400 rows -> 4 tiles; seq 1: 200 x 4 = 800 -> 7 tiles
+    assert info.num_items == 4 + 7 and info.num_merge_rows == 0 and info.num_partials == 0
+    a2, _k2 = _args(split_keys_prefill=1024)
+    st, info = _plan(a2)
+    # seq 0 kv 1100 -> 2 splits; seq 1 kv 200 -> 1
+    assert st == 0 and info.num_items == 4 * 2 + 7 and info.num_merge_rows == 100
+    assert info.num_partials == 2 * 100 * 32
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, _lib.CPA_ERR_UNSUPPORTED),
+    ("num_kv_heads", 5, _lib.CPA_ERR_INVALID_ARG),          # 32 % 5 != 0
+    ("kv_segment_size", 768, _lib.CPA_ERR_INVALID_ARG),     # not in {512,...,4096}
+    ("block_size", 12, _lib.CPA_ERR_UNSUPPORTED),
+    ("max_blocks_per_seq", 60, _lib.CPA_ERR_INVALID_ARG),  # 1100 tokens need 69 blocks
+    ("split_keys_prefill", 1000, _lib.CPA_ERR_INVALID_ARG),  # not a multiple of S
+    ("num_seqs", 0, _lib.CPA_ERR_INVALID_ARG),
+    ("dtype", 7, _lib.CPA_ERR_INVALID_ARG),
+])
+def test_bad_arguments_are_refused(field, value, code):
+    a, _keep = _args(**{field: value})
+    assert _plan(a)[0] == code
+    assert _lib.lib().cpa_prepare(ctypes.byref(a), None) == code
+    assert _lib.lib().cpa_attention(ctypes.byref(a), None) == code
+
+
+def test_bad_host_mirrors_are_refused():
+    a, _k = _args(cu=[0, 100, 299])                  # does not end at total_q
+    assert _plan(a)[0] == _lib.CPA_ERR_INVALID_ARG
+    a, _k = _args(cu=[0, 200, 100], total_q=100)    # decreasing
+    assert _plan(a)[0] == _lib.CPA_ERR_INVALID_ARG
+    a, _k = _args(cached=[-1, 0])
+    assert _plan(a)[0] == _lib.CPA_ERR_INVALID_ARG
+    a, _k = _args(kv_segment_size=0)                 # no segments but cached KV present
+    assert _plan(a)[0] == _lib.CPA_ERR_INVALID_ARG
+
+
+def test_missing_workspace_is_refused_before_launch():
+    a, _keep = _args()
+    a.workspace, a.workspace_bytes = 0, 0
+    assert _lib.lib().cpa_prepare(ctypes.byref(a), None) == _lib.CPA_ERR_WORKSPACE
+    st, info = _plan(a)
+    a.workspace, a.workspace_bytes = 0x1000, info.workspace_bytes - 1
+    assert _lib.lib().cpa_attention(ctypes.byref(a), None) == _lib.CPA_ERR_WORKSPACE
+
+
+def test_fp32_head_dim_128_is_unsupported():
+    a, _keep = _args(dtype=1)
+    assert _lib.lib().cpa_check_args(ctypes.byref(a)) == _lib.CPA_ERR_UNSUPPORTED

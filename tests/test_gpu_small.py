@@ -1,0 +1,162 @@
+"""GPU parity on small and ragged batches: every output element against the
+oracle, every cache byte against the oracle's expected pool."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_helpers import (DEV, Pair, assert_close, bits_of, gpu_call, need_gpu, quantize,
+                               say)
+
+pytestmark = pytest.mark.gpu
+
+# name, dtype, H, G, D, bs, S, partial requests [(prompt, computed)], decodes [ctx], budget
+CASES = [
+    ("c0_single", "bf16", 8, 2, 128, 16, 512, [(300, 0)], [], 4096),
+    ("ragged_multi", "bf16", 32, 8, 128, 16, 1024, [(1500, 1000), (17, 0), (600, 511), (2100, 2048)],
+     [], 8192),
+    ("hpg1_d64", "bf16", 4, 4, 64, 8, 512, [(700, 300), (129, 64)], [], 4096),
+    ("hpg8", "bf16", 64, 8, 128, 16, 512, [(900, 700)], [], 4096),
+    ("bs128", "bf16", 32, 8, 128, 128, 1024, [(3000, 2048), (130, 0)], [], 4096),
+    ("fp32_c1like", "fp32", 4, 4, 64, 16, 512, [(1024, 768)], [], 256),
+    ("fp32_hpg2", "fp32", 8, 4, 64, 32, 512, [(400, 111), (65, 0)], [], 4096),
+    ("mixed_decodes", "bf16", 32, 8, 128, 16, 512, [(1300, 1024)], [1, 15, 16, 17, 600, 1111, 2049],
+     8192),
+    ("tiny_rows", "bf16", 32, 8, 128, 16, 512, [(2, 1), (1, 0), (64, 63)], [], 4096),
+]
+SPLITS = {"auto": (0, 0), "never": (-1, -1), "seg": ("S", "S"), "seg2": ("2S", "S")}
+
+
+def _resolve(v, S):
+    return {"S": S, "2S": 2 * S}.get(v, v)
+
+
+def run_case(case, split, fill=0.0, seed=0):
+    name, dtype, H, G, D, bs, S, reqs, decodes, budget = case
+    rng = np.random.default_rng(1000 + seed)
+    max_blocks = max(-(-(p + 1) // bs) for p, _ in reqs + [(c + 1, 0) for c in decodes]) + 1
+    need = sum(-(-p // bs) for p, _ in reqs) + sum(-(-(c + 1) // bs) for c in decodes)
+    nb = need + 37
+    order = rng.permutation(nb).astype(np.int32)
+    pair = Pair(nb, G, bs, D, dtype, budget, max_blocks, order, fill=fill)
+    rid = 0
+    for ctx in decodes:
+        pair.add_decode(rid, ctx)
+        k64 = rng.standard_normal((ctx, G, D)).astype(np.float32)
+        v64 = rng.standard_normal((ctx, G, D)).astype(np.float32)
+        kt, kq = quantize(k64, dtype)
+        vt, vq = quantize(v64, dtype)
+        pair.fill_context(rid, kq, vq, kt, vt)
+        rid += 1
+    for prompt, computed in reqs:
+        pair.add_partial(rid, prompt, computed)
+        if computed:
+            kt, kq = quantize(rng.standard_normal((computed, G, D)), dtype)
+            vt, vq = quantize(rng.standard_normal((computed, G, D)), dtype)
+            pair.fill_context(rid, kq, vq, kt, vt)
+        rid += 1
+    pb, ob = pair.step()
+    T = pb["num_tokens"]
+    qt, q64 = quantize(rng.standard_normal((T, H, D)), dtype)
+    kt, k64 = quantize(rng.standard_normal((T, G, D)), dtype)
+    vt, v64 = quantize(rng.standard_normal((T, G, D)), dtype)
+    sp, sd = (_resolve(x, S) for x in SPLITS[split])
+    say(f"case {name} split={split} T={T} seqs={pb['num_seqs']}")
+    out, _ = gpu_call(pair.cache, pb, qt, kt, vt, S, split_pre=sp, split_dec=sd)
+    ref = pair.oracle_batch(ob, q64, k64, v64, 1 / math.sqrt(D), G)
+    return pair, out, ref, dtype
+
+
+@pytest.mark.parametrize("split", list(SPLITS))
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_small_batches_match_oracle(case, split):
+    need_gpu()
+    pair, out, ref, dtype = run_case(case, split)
+    assert_close(out.to(torch.float64).numpy(), ref, dtype, f"{case[0]}/{split}")
+    # every cache byte: written slots hold the new rows, all others untouched
+    gk, gv = pair.cache.canonical_bits()
+    assert np.array_equal(gk, bits_of(pair.k_pool, dtype))
+    assert np.array_equal(gv, bits_of(pair.v_pool, dtype))
+
+
+@pytest.mark.parametrize("case", [CASES[1], CASES[7], CASES[6]], ids=["ragged", "decodes", "fp32"])
+def test_stale_nan_slots_never_leak(case):
+    # every slot not written so far is NaN: unreferenced blocks and the unused
+    # tail of each sequence's last block
+    need_gpu()
+    pair, out, ref, dtype = run_case(case, "seg", fill=float("nan"))
+    assert_close(out.to(torch.float64).numpy(), ref, dtype, f"{case[0]}/nan")
+
+
+def test_selector_queries_select_exact_value_rows():
+    """Bit-exact check of every index path through attention: q = alpha*k[tau]
+    with unit keys gives a logit margin above 100, so P rounds to one-hot and
+    out[t, h] must equal V[tau] bit for bit."""
+    need_gpu()
+    H, G, D, bs, S = 32, 8, 128, 16, 1024
+    rng = np.random.default_rng(7)
+    computed, n = 3000, 700
+    L = computed + n
+    k = rng.standard_normal((L, G, D))
+    k /= np.linalg.norm(k, axis=2, keepdims=True)
+    kt, k64 = quantize(k, "bf16")
+    vt, v64 = quantize(rng.standard_normal((L, G, D)), "bf16")
+    nb = -(-L // bs) + 20
+    pair = Pair(nb, G, bs, D, "bf16", 4096, -(-L // bs) + 1, rng.permutation(nb).astype(np.int32))
+    pair.add_partial(0, L, computed)
+    pair.fill_context(0, k64[:computed], v64[:computed], kt[:computed], vt[:computed])
+    pb, ob = pair.step()
+    tau = np.zeros((n, H), dtype=np.int64)
+    q = np.zeros((n, H, D))
+    for t in range(n):
+        for h in range(H):
+            tau[t, h] = (t * 7919 + h * 104729) % (computed + t + 1)
+            q[t, h] = 2000.0 * k64[tau[t, h], h // (H // G)]
+    qt, _ = quantize(q, "bf16")
+    out, _ = gpu_call(pair.cache, pb, qt, kt[computed:], vt[computed:], S)
+    got = out.view(torch.int16).numpy()
+    want = vt.view(torch.int16).numpy()
+    for h in range(H):
+        assert np.array_equal(got[:, h], want[tau[:, h], h // (H // G)]), f"head {h}"
+    # every physical block of the sequence was selected at least once
+    rows = ob["block_table"][0]
+    hit = {rows[p // bs] for p in np.unique(tau)}
+    assert len(hit) == -(-L // bs)
+
+
+def test_empty_sequence_in_batch_and_lse():
+    """A batch with a zero-length sequence between two real ones; the optional
+    log-sum-exp output matches the closed form for K = 0 (log of the number of
+    visible keys), unsplit and split at 512 keys (which goes through the merge)."""
+    need_gpu()
+    H, G, D, bs, S = 8, 2, 128, 16, 512
+    rng = np.random.default_rng(3)
+    pair = Pair(80, G, bs, D, "bf16", 4096, 60, rng.permutation(80).astype(np.int32))
+    pair.add_partial(0, 800, 600)
+    kz = torch.zeros((600, G, D), dtype=torch.bfloat16)
+    pair.fill_context(0, np.zeros((600, G, D)), np.zeros((600, G, D)), kz, kz)
+    pair.add_partial(1, 50, 0)
+    pb, ob = pair.step()
+    # insert an empty sequence by hand (same slots; cu repeats an offset)
+    batch = dict(pb)
+    batch["cu_seqlens_q"] = np.array([0, 200, 200, 250], np.int32)
+    batch["cached_seq_len"] = np.array([600, 0, 0], np.int32)
+    batch["block_table"] = np.stack([pb["block_table"][0], pb["block_table"][1], pb["block_table"][1]])
+    T = 250
+    qt, _ = quantize(rng.standard_normal((T, H, D)), "bf16")
+    kt = torch.zeros((T, G, D), dtype=torch.bfloat16)
+    vt, v64 = quantize(rng.standard_normal((T, G, D)), "bf16")
+    for sp in (-1, 512):
+        out, lse = gpu_call(pair.cache, batch, qt, kt, vt, S, want_lse=True, split_pre=sp)
+        visible = np.concatenate([600 + np.arange(1, 201), np.arange(1, 51)])
+        np.testing.assert_allclose(lse.numpy(), np.log(visible)[None, :].repeat(H, 0), rtol=0, atol=1e-5)
+        # K = 0: output is the running mean of V over the visible positions
+        ctx_v = np.zeros((600, G, D))
+        seq0 = np.concatenate([ctx_v, v64[:200]])
+        mean0 = np.cumsum(seq0, axis=0)[600:] / np.arange(601, 801)[:, None, None]
+        mean1 = np.cumsum(v64[200:], axis=0) / np.arange(1, 51)[:, None, None]
+        want = np.concatenate([mean0, mean1])
+        got = out.to(torch.float64).numpy()
+        for h in range(H):
+            assert np.abs(got[:, h] - want[:, h // (H // G)]).max() <= 2e-2

@@ -150,7 +150,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     constexpr int NQF = D / (2 * KPL);              // Q fragments (k-steps over D)
     constexpr int NKS = kKeys / (2 * KPL);          // PV k-steps per tile
     constexpr int NDT = D / 32;                     // 32-row tiles of O^T
-    constexpr int QCH = (D / 2) / EPC;              // 16-B chunks in a lane's half row of Q
     static_assert(NLD * kThreads == kKeys * NCK, "tile must split evenly over threads");
 
     __shared__ __attribute__((aligned(16))) T lds_k[2][kKeys * D];
@@ -198,21 +197,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     const int bs = p.block_size;
     const int lbs = p.log2_bs;
 
-    // Q: lane holds elements [half*D/2, half*D/2 + D/2) of its row
-    u32x4 qc[QCH];
+    // Q: lane holds elements [half*D/2, half*D/2 + D/2) of its row, as the
+    // B-operand fragments of the NQF k-steps over D (fragment f covers
+    // elements half*D/2 + f*KPL .. + KPL-1)
+    Frag qf[NQF];
     {
         const T* qp = (const T*)p.q + ((size_t)(q0 + t) * p.num_heads + head) * D + half * (D / 2);
 #pragma unroll
-        for (int i = 0; i < QCH; ++i)
-            qc[i] = row_ok ? *(const u32x4*)(qp + i * EPC) : u32x4{0u, 0u, 0u, 0u};
-    }
-    auto qfrag = [&](int f) -> Frag {
-        if constexpr (KPL == 8) {
-            return __builtin_bit_cast(Frag, qc[f]);
-        } else {
-            return __builtin_bit_cast(float, qc[f / 4][f % 4]);
+        for (int f = 0; f < NQF; ++f) {
+            if constexpr (KPL == 8) {
+                qf[f] = row_ok ? *(const Frag*)(qp + f * KPL) : Frag{};
+            } else {
+                qf[f] = row_ok ? qp[f] : 0.f;
+            }
         }
-    };
+    }
 
     float m_run = -INFINITY;
     float l_run = 0.f;
@@ -282,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                 const int e = half * (D / 2) + f * KPL;
                 const int ch = e / EPC, within = e % EPC;
                 const Frag a = *(const Frag*)(kb + (ch ^ sw) * EPC + within);
-                sacc[sub] = E::mma(a, qfrag(f), sacc[sub]);
+                sacc[sub] = E::mma(a, qf[f], sacc[sub]);
             }
         }
         // register r of block sub holds key ts + sub*32 + 16*(r/8) + 8*half + r%8

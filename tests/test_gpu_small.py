@@ -108,10 +108,22 @@ def test_selector_queries_select_exact_value_rows():
     pair.fill_context(0, k64[:computed], v64[:computed], kt[:computed], vt[:computed])
     pb, ob = pair.step()
     tau = np.zeros((n, H), dtype=np.int64)
-    q = np.zeros((n, H, D))
     for t in range(n):
         for h in range(H):
             tau[t, h] = (t * 7919 + h * 104729) % (computed + t + 1)
+    # make sure every block of the sequence is picked by some (token, head)
+    pinned = set()
+    for i in range(-(-L // bs)):
+        p = min(i * bs + i % bs, L - 1)
+        t, h = max(i, p - computed), i % H
+        while (t, h) in pinned:
+            h = (h + 1) % H
+            t = t + 1 if h == i % H else t
+        pinned.add((t, h))
+        tau[t, h] = p
+    q = np.zeros((n, H, D))
+    for t in range(n):
+        for h in range(H):
             q[t, h] = 2000.0 * k64[tau[t, h], h // (H // G)]
     qt, _ = quantize(q, "bf16")
     out, _ = gpu_call(pair.cache, pb, qt, kt[computed:], vt[computed:], S)

@@ -220,7 +220,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     for (int i = 0; i < NDT; ++i) oacc[i] = f32x16{};
 
     u32x4 kreg[NLD], vreg[NLD];
-    auto load_tile = [&](int ts) {
+    const uint32_t nb_max = (uint32_t)p.num_blocks - 1;
+    // Guarded gather for the tile that reaches the end of the sequence: keys
+    // at or past kv_len are zero-filled, V^T chunks straddling it are masked.
+    auto load_tile_edge = [&](int ts) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int cidx = i * kThreads + tid;
@@ -228,10 +231,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             const int j = ts + key;
             u32x4 val = {0u, 0u, 0u, 0u};
             if (j < kv_len) {
-                const int blk = bt[j >> lbs];
-                if ((unsigned)blk < (unsigned)p.num_blocks)
-                    val = *(const u32x4*)(kc + (((size_t)blk * G + g) * bs + (j & (bs - 1))) * D +
-                                          ch * EPC);
+                const uint32_t blk = min((uint32_t)bt[j >> lbs], nb_max);
+                val = *(const u32x4*)(kc + (((size_t)blk * G + g) * bs + (j & (bs - 1))) * D + ch * EPC);
             }
             kreg[i] = val;
         }
@@ -242,14 +243,50 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             const int j = ts + kcn * EPC;
             u32x4 val = {0u, 0u, 0u, 0u};
             if (j < kv_len) {
-                const int blk = bt[j >> lbs];
-                if ((unsigned)blk < (unsigned)p.num_blocks) {
-                    val = *(const u32x4*)(vc + (((size_t)blk * G + g) * D + d) * bs + (j & (bs - 1)));
-                    if (kv_len - j < EPC) val = keep_first<T>(val, kv_len - j);
-                }
+                const uint32_t blk = min((uint32_t)bt[j >> lbs], nb_max);
+                val = *(const u32x4*)(vc + (((size_t)blk * G + g) * D + d) * bs + (j & (bs - 1)));
+                if (kv_len - j < EPC) val = keep_first<T>(val, kv_len - j);
             }
             vreg[i] = val;
         }
+    };
+    // Unguarded gather for tiles whose 64 keys all exist.  Thread tid always
+    // loads K rows tid/NCK + i*KROWS (chunk tid%NCK) and V^T rows
+    // tid/NCV + i*VROWS (key chunk tid%NCV).  When a load instruction's
+    // KROWS rows lie in one block (block_size >= KROWS) the block id is
+    // wave-uniform and the address is a scalar base plus a per-thread
+    // constant.  Block ids are clamped into the pool.
+    constexpr int KROWS = kThreads / NCK;
+    constexpr int VROWS = kThreads / NCV;
+    const int k_row = tid / NCK, k_ch = tid % NCK;
+    const int v_row = tid / NCV, v_kc = tid % NCV;
+    const size_t k_lane_off = (size_t)k_row * D + k_ch * EPC;
+    auto load_tile_full = [&](int ts) {
+        if (bs >= KROWS) {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int j0 = ts + i * KROWS;
+                const uint32_t blk = min((uint32_t)bt[j0 >> lbs], nb_max);
+                const T* base = kc + (((size_t)blk * G + g) * bs + (j0 & (bs - 1))) * D;
+                kreg[i] = *(const u32x4*)(base + k_lane_off);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int j = ts + i * KROWS + k_row;
+                const uint32_t blk = min((uint32_t)bt[j >> lbs], nb_max);
+                kreg[i] = *(const u32x4*)(kc + (((size_t)blk * G + g) * bs + (j & (bs - 1))) * D +
+                                          k_ch * EPC);
+            }
+        }
+        const int j = ts + v_kc * EPC;
+        const uint32_t blk = min((uint32_t)bt[j >> lbs], nb_max);
+        const T* vbase = vc + (((size_t)blk * G + g) * D + v_row) * bs + (j & (bs - 1));
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) vreg[i] = *(const u32x4*)(vbase + (size_t)i * VROWS * bs);
+    };
+    auto load_tile = [&](int ts) {
+        if (ts + kKeys <= kv_len) load_tile_full(ts); else load_tile_edge(ts);
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
@@ -268,8 +305,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
         }
     };
 
+    const float sl2e = p.scale_log2;
     auto compute = [&](int buf, int ts) {
-        // S^T = K Q^T for two 32-key blocks
+        // S^T = K Q^T for two 32-key blocks (raw, unscaled scores)
         f32x16 sacc[2];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
@@ -285,39 +323,48 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             }
         }
         // register r of block sub holds key ts + sub*32 + 16*(r/8) + 8*half + r%8
-        const bool need_mask = (ts + kKeys - 1 > c + wt_min) || (ts + kKeys > k1);
+        if ((ts + kKeys - 1 > c + wt_min) || (ts + kKeys > k1)) {
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = ts + sub * 32 + ((r >> 3) << 4) + (half << 3) + (r & 7);
+                    if (j > lim || j >= k1) sacc[sub][r] = -INFINITY;
+                }
+            }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = sacc[sub][r] * p.scale_log2;
-                if (need_mask) {
-                    const int j = ts + sub * 32 + ((r >> 3) << 4) + (half << 3) + (r & 7);
-                    if (j > lim || j >= k1) x = -INFINITY;
-                }
-                sacc[sub][r] = x;
-                mx = fmaxf(mx, x);
-            }
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sub][r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        // Lazy rescaling: the row's reference maximum moves only when the
+        // tile maximum exceeds it by more than 8 (log2 units), so most tiles
+        // skip the O rescale; exp2 arguments stay <= 8.  (-inf - -inf is NaN,
+        // which compares false: an all-masked row keeps its -inf reference.)
+        const bool grow = (mx - m_run) * sl2e > 8.f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * sl2e) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
+            m_run = m_new;
+        }
+        const float nm = (m_run == -INFINITY) ? 0.f : -m_run * sl2e;
         float rs = 0.f;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float pv = __builtin_amdgcn_exp2f(sacc[sub][r] - m_use);
+                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sub][r], sl2e, nm));
                 sacc[sub][r] = pv;
                 rs += pv;
             }
         }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
+        l_run += rs;
 
         // P^T fragments for the PV k-steps
         Frag pf[NKS];
@@ -394,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             }
         }
         if (p.lse && half == 0)
-            p.lse[(size_t)head * p.total_q + q0 + t] = (m_run + __log2f(l_tot)) * kLn2;
+            p.lse[(size_t)head * p.total_q + q0 + t] = (m_run * sl2e + __log2f(l_tot)) * kLn2;
     } else {
         const size_t pidx = (size_t)p.seq_info[b].z + ((size_t)split * n + t) * p.num_heads + head;
         float* po = p.part_o + pidx * D;
@@ -409,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                 *(f32x4*)(po + d) = v;
             }
         }
-        if (half == 0) p.part_ml[pidx] = make_float2(m_run, l_tot);
+        if (half == 0) p.part_ml[pidx] = make_float2(m_run * sl2e, l_tot);
     }
 }
 
@@ -681,7 +728,7 @@ cpa_status resolve(const cpa_attn_args* a, Resolved* r) {
     if (a->num_seqs <= 0 || a->num_heads <= 0 || a->max_blocks_per_seq <= 0) return CPA_ERR_INVALID_ARG;
     if (a->num_seqs > kMaxSeqs) return CPA_ERR_UNSUPPORTED;
     if (a->num_heads % a->num_kv_heads != 0) return CPA_ERR_INVALID_ARG;
-    if (!std::isfinite(a->scale)) return CPA_ERR_INVALID_ARG;
+    if (!std::isfinite(a->scale) || !(a->scale > 0.f)) return CPA_ERR_INVALID_ARG;
     const int S = a->kv_segment_size;
     if (S != 0 && S != 512 && S != 1024 && S != 2048 && S != 4096) return CPA_ERR_INVALID_ARG;
     if (S != 0 && S % a->block_size != 0) return CPA_ERR_INVALID_ARG;

@@ -98,7 +98,7 @@ typedef struct cpa_attn_args {
                                        0 automatic, -1 never split, else a
                                        multiple of kv_segment_size              */
     int32_t split_keys_decode;      /* same for decode rows (0: one segment)    */
-    float   scale;                  /* softmax scale, usually 1/sqrt(D)         */
+    float   scale;                  /* softmax scale > 0, usually 1/sqrt(D)     */
     const void* q;                  /* device                                   */
     const void* k_new;              /* device                                   */
     const void* v_new;              /* device                                   */

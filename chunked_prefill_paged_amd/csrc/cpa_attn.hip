@@ -250,43 +250,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             vreg[i] = val;
         }
     };
-    // Unguarded gather for tiles whose 64 keys all exist.  Thread tid always
-    // loads K rows tid/NCK + i*KROWS (chunk tid%NCK) and V^T rows
-    // tid/NCV + i*VROWS (key chunk tid%NCV).  When a load instruction's
-    // KROWS rows lie in one block (block_size >= KROWS) the block id is
-    // wave-uniform and the address is a scalar base plus a per-thread
-    // constant.  Block ids are clamped into the pool.
-    constexpr int KROWS = kThreads / NCK;
-    constexpr int VROWS = kThreads / NCV;
-    const int k_row = tid / NCK, k_ch = tid % NCK;
-    const int v_row = tid / NCV, v_kc = tid % NCV;
-    const size_t k_lane_off = (size_t)k_row * D + k_ch * EPC;
-    auto load_tile_full = [&](int ts) {
-        if (bs >= KROWS) {
+    // Full tiles (all 64 keys exist) are gathered straight into LDS with
+    // global_load_lds_dwordx4: one instruction fills a 1 KiB slab, lane L's
+    // 16 bytes landing at slab + 16*L.  Each lane therefore fetches the
+    // global chunk that belongs at its (swizzled) slot.  K slab s holds rows
+    // s*RK.., V^T slab s holds rows d = s*RV..; wave w fills slabs
+    // w*NLD .. w*NLD+NLD-1 of both.  The RK rows of a K slab always share a
+    // block (block_size >= 8 >= RK), so its block id is wave-uniform.
+    constexpr int RK = 64 / NCK;
+    constexpr int RV = 64 / NCV;
+    static_assert(RK <= 8, "K slab rows must fit the smallest block");
+    int k_dma_off[NLD], v_dma_d[NLD], v_dma_key[NLD];
 #pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const int j0 = ts + i * KROWS;
-                const uint32_t blk = min((uint32_t)bt[j0 >> lbs], nb_max);
-                const T* base = kc + (((size_t)blk * G + g) * bs + (j0 & (bs - 1))) * D;
-                kreg[i] = *(const u32x4*)(base + k_lane_off);
-            }
-        } else {
+    for (int i = 0; i < NLD; ++i) {
+        const int sl = wave * NLD + i;
+        const int rk = sl * RK + lane / NCK;
+        k_dma_off[i] = (lane / NCK) * D + ((lane % NCK) ^ (swap_bits23(rk & 31) & SWK)) * EPC;
+        const int d = sl * RV + lane / NCV;
+        v_dma_d[i] = d;
+        v_dma_key[i] = ((lane % NCV) ^ (((d & 7) ^ ((d >> 3) & 1)) & SWV)) * EPC;
+    }
+    auto dma_tile = [&](int ts, int buf) {
 #pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const int j = ts + i * KROWS + k_row;
-                const uint32_t blk = min((uint32_t)bt[j >> lbs], nb_max);
-                kreg[i] = *(const u32x4*)(kc + (((size_t)blk * G + g) * bs + (j & (bs - 1))) * D +
-                                          k_ch * EPC);
-            }
+        for (int i = 0; i < NLD; ++i) {
+            const int sl = wave * NLD + i;
+            const int j0 = ts + sl * RK;
+            const uint32_t blk = min((uint32_t)bt[j0 >> lbs], nb_max);
+            const T* src = kc + (((size_t)blk * G + g) * bs + (j0 & (bs - 1))) * D + k_dma_off[i];
+            __builtin_amdgcn_global_load_lds((const void*)src, (void*)((char*)&lds_k[buf][0] + sl * 1024),
+                                             16, 0, 0);
         }
-        const int j = ts + v_kc * EPC;
-        const uint32_t blk = min((uint32_t)bt[j >> lbs], nb_max);
-        const T* vbase = vc + (((size_t)blk * G + g) * D + v_row) * bs + (j & (bs - 1));
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) vreg[i] = *(const u32x4*)(vbase + (size_t)i * VROWS * bs);
-    };
-    auto load_tile = [&](int ts) {
-        if (ts + kKeys <= kv_len) load_tile_full(ts); else load_tile_edge(ts);
+        for (int i = 0; i < NLD; ++i) {
+            const int sl = wave * NLD + i;
+            const int j = ts + v_dma_key[i];
+            const uint32_t blk = min((uint32_t)bt[j >> lbs], nb_max);
+            const T* src = vc + (((size_t)blk * G + g) * D + v_dma_d[i]) * bs + (j & (bs - 1));
+            __builtin_amdgcn_global_load_lds((const void*)src, (void*)((char*)&lds_v[buf][0] + sl * 1024),
+                                             16, 0, 0);
+        }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
@@ -405,14 +407,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     if (kend > k0) {
         const int tile0 = k0 / kKeys;
         const int ntiles = (kend - k0 + kKeys - 1) / kKeys;
-        load_tile(tile0 * kKeys);
-        store_tile(0);
+        if (tile0 * kKeys + kKeys <= kv_len) dma_tile(tile0 * kKeys, 0);
         for (int it = 0; it < ntiles; ++it) {
             const int ts = (tile0 + it) * kKeys;
-            if (it + 1 < ntiles) load_tile(ts + kKeys);
+            const int buf = it & 1;
+            if (ts + kKeys > kv_len) {       // the sequence's last tile: guarded, through registers
+                load_tile_edge(ts);
+                store_tile(buf);
+            }
+            // this tile's gathers have landed (each wave waits for its own,
+            // the barrier for everyone's); all waves are done with buf ^ 1
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            if (wave_on && ts <= c + wt_max) compute(it & 1, ts);
-            if (it + 1 < ntiles) store_tile((it + 1) & 1);
+            if (it + 1 < ntiles && ts + 2 * kKeys <= kv_len) dma_tile(ts + kKeys, buf ^ 1);
+            if (wave_on && ts <= c + wt_max) compute(buf, ts);
         }
     }
 

@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
         v_dma_d[i] = d;
         v_dma_key[i] = ((lane % NCV) ^ (((d & 7) ^ ((d >> 3) & 1)) & SWV)) * EPC;
     }
-    auto dma_tile = [&](int ts, int buf) {
+    auto dma_k = [&](int ts, int buf) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int sl = wave * NLD + i;
@@ -280,6 +280,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             __builtin_amdgcn_global_load_lds((const void*)src, (void*)((char*)&lds_k[buf][0] + sl * 1024),
                                              16, 0, 0);
         }
+    };
+    auto dma_v = [&](int ts, int buf) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int sl = wave * NLD + i;
@@ -308,30 +310,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     };
 
     const float sl2e = p.scale_log2;
-    auto compute = [&](int buf, int ts) {
-        // S^T = K Q^T for two 32-key blocks (raw, unscaled scores)
-        f32x16 sacc[2];
+    typedef f32x16 Scores[2];   // S^T of one 64-key tile: two 32-key blocks
+
+    // S^T = K Q^T (raw, unscaled scores) from K buffer kbuf
+    auto qk = [&](int kbuf, Scores& S) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-            sacc[sub] = f32x16{};
-            const T* kb = &lds_k[buf][(sub * 32 + swap_bits23(lrow)) * D];
+            S[sub] = f32x16{};
+            const T* kb = &lds_k[kbuf][(sub * 32 + swap_bits23(lrow)) * D];
             const int sw = lane & SWK;
 #pragma unroll
             for (int f = 0; f < NQF; ++f) {
                 const int e = half * (D / 2) + f * KPL;
                 const int ch = e / EPC, within = e % EPC;
                 const Frag a = *(const Frag*)(kb + (ch ^ sw) * EPC + within);
-                sacc[sub] = E::mma(a, qf[f], sacc[sub]);
+                S[sub] = E::mma(a, qf[f], S[sub]);
             }
         }
-        // register r of block sub holds key ts + sub*32 + 16*(r/8) + 8*half + r%8
+    };
+    // Causal / split-end mask (boundary tiles only), then the row maximum.
+    // Register r of block sub holds key ts + sub*32 + 16*(r/8) + 8*half + r%8.
+    auto mask_max = [&](int ts, Scores& S) -> float {
         if ((ts + kKeys - 1 > c + wt_min) || (ts + kKeys > k1)) {
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int j = ts + sub * 32 + ((r >> 3) << 4) + (half << 3) + (r & 7);
-                    if (j > lim || j >= k1) sacc[sub][r] = -INFINITY;
+                    if (j > lim || j >= k1) S[sub][r] = -INFINITY;
                 }
             }
         }
@@ -339,13 +345,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sub][r]);
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[sub][r]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // Lazy rescaling: the row's reference maximum moves only when the
-        // tile maximum exceeds it by more than 8 (log2 units), so most tiles
-        // skip the O rescale; exp2 arguments stay <= 8.  (-inf - -inf is NaN,
-        // which compares false: an all-masked row keeps its -inf reference.)
+        return fmaxf(mx, __shfl_xor(mx, 32));
+    };
+    // Lazy rescaling: the row's reference maximum moves only when a tile's
+    // maximum exceeds it by more than 8 (log2 units), so most tiles skip the
+    // O rescale and exp2 arguments stay <= 8.  (-inf - -inf is NaN, which
+    // compares false: an all-masked row keeps its -inf reference.)
+    auto update_ref = [&](float mx) {
         const bool grow = (mx - m_run) * sl2e > 8.f;
         if (__builtin_amdgcn_ballot_w64(grow)) {
             const float m_new = grow ? mx : m_run;
@@ -355,38 +363,40 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
             m_run = m_new;
         }
+    };
+    // P = exp2(S*scale*log2e - m), row sums, and the P^T fragments of PV
+    auto probs = [&](Scores& S, Frag (&pf)[NKS]) {
         const float nm = (m_run == -INFINITY) ? 0.f : -m_run * sl2e;
         float rs = 0.f;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sub][r], sl2e, nm));
-                sacc[sub][r] = pv;
+                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[sub][r], sl2e, nm));
+                S[sub][r] = pv;
                 rs += pv;
             }
         }
         l_run += rs;
-
-        // P^T fragments for the PV k-steps
-        Frag pf[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             if constexpr (KPL == 8) {
                 const int sub = ks >> 1, r0 = (ks & 1) * 8;
                 bf16x8 v;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = (__bf16)sacc[sub][r0 + i];
+                for (int i = 0; i < 8; ++i) v[i] = (__bf16)S[sub][r0 + i];
                 pf[ks] = v;
             } else {
-                pf[ks] = sacc[ks >> 4][ks & 15];
+                pf[ks] = S[ks >> 4][ks & 15];
             }
         }
-        // O^T += V^T P^T
+    };
+    // O^T += V^T P^T from V buffer vbuf
+    auto pv = [&](int vbuf, const Frag (&pf)[NKS]) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             const int drow = dt * 32 + lrow;
-            const T* vb = &lds_v[buf][drow * kKeys];
+            const T* vb = &lds_v[vbuf][drow * kKeys];
             const int sw = ((drow & 7) ^ ((drow >> 3) & 1)) & SWV;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -403,24 +413,71 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             }
         }
     };
+    auto active = [&](int ts) { return wave_on && ts <= c + wt_max; };
 
+    // Tiles [tile0, tile0 + ntiles) cover keys [k0, kend).  The first nfull
+    // have all 64 keys in the sequence and run software-pipelined: while the
+    // exp/sum/convert of tile u runs on the VALU, the MFMAs compute S of tile
+    // u+1; while PV of tile u runs, the VALU masks and reduces S of tile u+1.
+    // K is gathered one tile ahead of V:
+    //   iteration u:  wait + barrier   (V(u), K(u+1) have landed; all waves
+    //                                   are done with V(u-1) and K(u))
+    //                 gather V(u+1) -> vbuf (u+1)%2, K(u+2) -> kbuf u%2
+    //                 P(u) from S(u)   ||  S(u+1) = K(u+1) Q^T
+    //                 O += V(u) P(u)   ||  mask + max of S(u+1)
+    // A last tile that reaches past the sequence end is then done on its own
+    // through guarded register loads.
     if (kend > k0) {
         const int tile0 = k0 / kKeys;
         const int ntiles = (kend - k0 + kKeys - 1) / kKeys;
-        if (tile0 * kKeys + kKeys <= kv_len) dma_tile(tile0 * kKeys, 0);
-        for (int it = 0; it < ntiles; ++it) {
-            const int ts = (tile0 + it) * kKeys;
-            const int buf = it & 1;
-            if (ts + kKeys > kv_len) {       // the sequence's last tile: guarded, through registers
-                load_tile_edge(ts);
-                store_tile(buf);
-            }
-            // this tile's gathers have landed (each wave waits for its own,
-            // the barrier for everyone's); all waves are done with buf ^ 1
+        const int nfull = min(ntiles, max(0, kv_len / kKeys - tile0));
+        Scores SA, SB;
+        Frag pf[NKS];
+        float mxA = -INFINITY, mxB = -INFINITY;
+        auto tstart = [&](int u) { return (tile0 + u) * kKeys; };
+        auto stage = [&](int u, Scores& Scur, float& mxcur, Scores& Snext, float& mxnext) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            if (it + 1 < ntiles && ts + 2 * kKeys <= kv_len) dma_tile(ts + kKeys, buf ^ 1);
-            if (wave_on && ts <= c + wt_max) compute(buf, ts);
+            if (u + 1 < nfull) dma_v(tstart(u + 1), (u + 1) & 1);
+            if (u + 2 < nfull) dma_k(tstart(u + 2), u & 1);
+            const bool act = active(tstart(u));
+            const bool act_next = u + 1 < nfull && active(tstart(u + 1));
+            if (act) {
+                update_ref(mxcur);
+                probs(Scur, pf);
+            }
+            if (act_next) qk((u + 1) & 1, Snext);
+            if (act) pv(u & 1, pf);
+            if (act_next) mxnext = mask_max(tstart(u + 1), Snext);
+        };
+        if (nfull > 0) {
+            dma_k(tstart(0), 0);
+            dma_v(tstart(0), 0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (nfull > 1) dma_k(tstart(1), 1);
+            if (active(tstart(0))) {
+                qk(0, SA);
+                mxA = mask_max(tstart(0), SA);
+            }
+            for (int u = 0; u < nfull; u += 2) {
+                stage(u, SA, mxA, SB, mxB);
+                if (u + 1 < nfull) stage(u + 1, SB, mxB, SA, mxA);
+            }
+        }
+        if (nfull < ntiles) {            // the edge tile
+            const int ts = tstart(nfull);
+            __syncthreads();             // every wave is done with both buffers
+            load_tile_edge(ts);
+            store_tile(0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (active(ts)) {
+                qk(0, SA);
+                update_ref(mask_max(ts, SA));
+                probs(SA, pf);
+                pv(0, pf);
+            }
         }
     }
 

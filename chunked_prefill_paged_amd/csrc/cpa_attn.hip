@@ -260,16 +260,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     constexpr int RK = 64 / NCK;
     constexpr int RV = 64 / NCV;
     static_assert(RK <= 8, "K slab rows must fit the smallest block");
-    int k_dma_off[NLD], v_dma_d[NLD], v_dma_key[NLD];
+    // Per-lane DMA source offsets: K slab i (row offset within the block-run
+    // and swizzled chunk) and V^T slab i (d row v_d0 + i*RV, key chunk whose
+    // swizzle depends only on the parity of the slab's 8-row group).
+    int k_dma_off[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-        const int sl = wave * NLD + i;
-        const int rk = sl * RK + lane / NCK;
+        const int rk = (wave * NLD + i) * RK + lane / NCK;
         k_dma_off[i] = (lane / NCK) * D + ((lane % NCK) ^ (swap_bits23(rk & 31) & SWK)) * EPC;
-        const int d = sl * RV + lane / NCV;
-        v_dma_d[i] = d;
-        v_dma_key[i] = ((lane % NCV) ^ (((d & 7) ^ ((d >> 3) & 1)) & SWV)) * EPC;
     }
+    const int v_d0 = wave * NLD * RV + lane / NCV;
+    auto v_dma_key = [&](int i) {
+        const int d = v_d0 + i * RV;
+        return ((lane % NCV) ^ (((d & 7) ^ ((d >> 3) & 1)) & SWV)) * EPC;
+    };
     auto dma_k = [&](int ts, int buf) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
@@ -285,9 +289,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int sl = wave * NLD + i;
-            const int j = ts + v_dma_key[i];
+            const int j = ts + v_dma_key(i);
             const uint32_t blk = min((uint32_t)bt[j >> lbs], nb_max);
-            const T* src = vc + (((size_t)blk * G + g) * D + v_dma_d[i]) * bs + (j & (bs - 1));
+            const T* src = vc + (((size_t)blk * G + g) * D + v_d0 + i * RV) * bs + (j & (bs - 1));
             __builtin_amdgcn_global_load_lds((const void*)src, (void*)((char*)&lds_v[buf][0] + sl * 1024),
                                              16, 0, 0);
         }
@@ -415,68 +419,185 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     };
     auto active = [&](int ts) { return wave_on && ts <= c + wt_max; };
 
+    // In bf16 with D = 128 every tile runs a hand-ordered sequence in half
+    // tiles of 32 keys (tiles on the causal diagonal, at a split end or at
+    // the sequence end first mask their scores to -inf).  LDS fragments are prefetched three MFMAs ahead through four
+    // rotating registers; sched_barrier fences pin the order:
+    //   P1  S0 = K[0:32] Q^T                 (8 MFMAs)
+    //   P2  S1 = K[32:64] Q^T                (8 MFMAs)  || max, exp, sum, convert of S0
+    //   P3  O += V[0:32] P0                  (8 MFMAs)  || max of S1
+    //   P4  O += V[32:64] P1                 (8 MFMAs)  || exp, sum, convert of S1
+    // The reference maximum of a row moves only when some lane's half-row
+    // maximum exceeds it by more than 8 (log2 units): the common path needs
+    // no exchange between the two lanes of a row; the rare path takes the
+    // row maximum and rescales O and l.  P0's PV is fully issued before S1's
+    // decision, so a rescale covers every product formed under the old
+    // reference.
+    constexpr bool kHandOrdered = (KPL == 8 && D == 128);
+    // LDS byte offsets of this lane's fragments: K fragment (k-step s8,
+    // 32-key block sb) at k_base + ((s8*16) ^ k_x) + sb*32*D*2; V fragment
+    // (k-step ks, d tile dt) at v_base + ((ks*32) ^ v_x) + dt*32*64*2.
+    uint32_t k_base = 0, k_x = 0, v_base = 0, v_x = 0;
+    if constexpr (kHandOrdered) {
+        k_base = (uint32_t)(swap_bits23(lrow) * D * 2 + ((half * 8) ^ (lane & 8)) * 16);
+        k_x = (uint32_t)((lane & 7) * 16);
+        const int swl = ((lrow & 7) ^ ((lrow >> 3) & 1)) & SWV;
+        v_base = (uint32_t)(lrow * kKeys * 2 + (half ^ (swl & 1)) * 16);
+        v_x = (uint32_t)((swl & 6) * 16);
+    }
+    auto compute_tile = [&](int buf, int ts, bool masked) {
+        if constexpr (kHandOrdered) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const char* kb = (const char*)&lds_k[buf][0];
+            const char* vb = (const char*)&lds_v[buf][0];
+            auto kfrag = [&](int f) {
+                return *(const bf16x8*)(kb + (k_base + (((f & 7) * 16) ^ k_x)) + (f >> 3) * (32 * D * 2));
+            };
+            auto vfrag = [&](int i) {
+                return *(const bf16x8*)(vb + (v_base + (((i >> 2) * 32) ^ v_x)) + (i & 3) * (32 * kKeys * 2));
+            };
+            // fragment j of the tile's 32 LDS reads: K fragments 0..15, then V 0..15
+            auto frag = [&](int j) { return j < 16 ? kfrag(j) : vfrag(j - 16); };
+            auto decide = [&](float hm) {
+                if (__builtin_amdgcn_ballot_w64((hm - m_run) * sl2e > 8.f)) {
+                    const float pm = fmaxf(hm, __shfl_xor(hm, 32));
+                    const bool g = (pm - m_run) * sl2e > 8.f;
+                    const float m_new = g ? pm : m_run;
+                    const float alpha = g ? __builtin_amdgcn_exp2f((m_run - m_new) * sl2e) : 1.f;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
+                    m_run = m_new;
+                }
+            };
+            f32x16 S0 = {}, S1 = {};
+            bf16x8 fr[4];
+            u32x4 pw[4];
+            float rs = 0.f;
+            // causal / split-end mask of one 32-key block (register r holds
+            // key ts + blk*32 + 16*(r/8) + 8*half + r%8)
+            auto apply_mask = [&](f32x16& S, int blk) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = ts + blk * 32 + ((r >> 3) << 4) + (half << 3) + (r & 7);
+                    if (j > lim || j >= k1) S[r] = -INFINITY;
+                }
+            };
+            // exp/sum/convert of two scores of S (registers r, r+1) into pw
+            auto ex2 = [&](const f32x16& S, int ks, int r, float nm) {
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2e, nm));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r + 1], sl2e, nm));
+                rs += e0 + e1;
+                const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+                pw[ks][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+            };
+            fr[0] = frag(0);
+            fr[1] = frag(1);
+            fr[2] = frag(2);
+            __builtin_amdgcn_sched_barrier(0);
+            // P1
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                fr[(f + 3) & 3] = frag(f + 3);
+                S0 = E::mma(fr[f & 3], qf[f], S0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (masked) apply_mask(S0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // P2: max of S0 under the first four S1 MFMAs
+            float hm = -INFINITY;
+#pragma unroll
+            for (int f = 8; f < 12; ++f) {
+                fr[(f + 3) & 3] = frag(f + 3);
+                S1 = E::mma(fr[f & 3], qf[f & 7], S1);
+                const int r = 4 * (f - 8);
+                hm = fmaxf(hm, fmaxf(fmaxf(S0[r], S0[r + 1]), fmaxf(S0[r + 2], S0[r + 3])));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            decide(hm);
+            float nm = (m_run == -INFINITY) ? 0.f : -m_run * sl2e;
+            __builtin_amdgcn_sched_barrier(0);
+            // P2: exp of S0 under the last four S1 MFMAs
+#pragma unroll
+            for (int f = 12; f < 16; ++f) {
+                fr[(f + 3) & 3] = frag(f + 3);
+                S1 = E::mma(fr[f & 3], qf[f & 7], S1);
+                const int r = 4 * (f - 12);
+                ex2(S0, r >> 3, r, nm);
+                ex2(S0, r >> 3, r + 2, nm);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            l_run += rs;                 // before S1's decision may rescale l
+            rs = 0.f;
+            if (masked) apply_mask(S1, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // P3: PV of the first half with the max of S1
+            hm = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                fr[(i + 3) & 3] = frag(16 + i + 3);
+                oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
+                hm = fmaxf(hm, fmaxf(S1[2 * i], S1[2 * i + 1]));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            decide(hm);
+            nm = (m_run == -INFINITY) ? 0.f : -m_run * sl2e;
+            __builtin_amdgcn_sched_barrier(0);
+            // P4: exp of S1 registers 0..7, then PV of keys 32..47 under the
+            // exp of registers 8..15, then PV of keys 48..63
+#pragma unroll
+            for (int r = 0; r < 8; r += 2) ex2(S1, 2, r, nm);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 8; i < 16; ++i) {
+                if (i + 3 < 16) fr[(i + 3) & 3] = frag(16 + i + 3);
+                oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
+                if (i < 12) ex2(S1, 3, 8 + 2 * (i - 8), nm);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            l_run += rs;
+        }
+    };
+
     // Tiles [tile0, tile0 + ntiles) cover keys [k0, kend).  The first nfull
-    // have all 64 keys in the sequence and run software-pipelined: while the
-    // exp/sum/convert of tile u runs on the VALU, the MFMAs compute S of tile
-    // u+1; while PV of tile u runs, the VALU masks and reduces S of tile u+1.
-    // K is gathered one tile ahead of V:
-    //   iteration u:  wait + barrier   (V(u), K(u+1) have landed; all waves
-    //                                   are done with V(u-1) and K(u))
-    //                 gather V(u+1) -> vbuf (u+1)%2, K(u+2) -> kbuf u%2
-    //                 P(u) from S(u)   ||  S(u+1) = K(u+1) Q^T
-    //                 O += V(u) P(u)   ||  mask + max of S(u+1)
-    // A last tile that reaches past the sequence end is then done on its own
-    // through guarded register loads.
+    // have all 64 keys in the sequence and are gathered straight into LDS,
+    // one tile ahead (double buffer, one barrier per tile); a last tile that
+    // reaches past the sequence end goes through guarded register loads.
     if (kend > k0) {
         const int tile0 = k0 / kKeys;
         const int ntiles = (kend - k0 + kKeys - 1) / kKeys;
         const int nfull = min(ntiles, max(0, kv_len / kKeys - tile0));
-        Scores SA, SB;
+        Scores S;
         Frag pf[NKS];
-        float mxA = -INFINITY, mxB = -INFINITY;
         auto tstart = [&](int u) { return (tile0 + u) * kKeys; };
-        auto stage = [&](int u, Scores& Scur, float& mxcur, Scores& Snext, float& mxnext) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (u + 1 < nfull) dma_v(tstart(u + 1), (u + 1) & 1);
-            if (u + 2 < nfull) dma_k(tstart(u + 2), u & 1);
-            const bool act = active(tstart(u));
-            const bool act_next = u + 1 < nfull && active(tstart(u + 1));
-            if (act) {
-                update_ref(mxcur);
-                probs(Scur, pf);
-            }
-            if (act_next) qk((u + 1) & 1, Snext);
-            if (act) pv(u & 1, pf);
-            if (act_next) mxnext = mask_max(tstart(u + 1), Snext);
-        };
         if (nfull > 0) {
             dma_k(tstart(0), 0);
             dma_v(tstart(0), 0);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (nfull > 1) dma_k(tstart(1), 1);
-            if (active(tstart(0))) {
-                qk(0, SA);
-                mxA = mask_max(tstart(0), SA);
-            }
-            for (int u = 0; u < nfull; u += 2) {
-                stage(u, SA, mxA, SB, mxB);
-                if (u + 1 < nfull) stage(u + 1, SB, mxB, SA, mxA);
-            }
         }
-        if (nfull < ntiles) {            // the edge tile
-            const int ts = tstart(nfull);
-            __syncthreads();             // every wave is done with both buffers
-            load_tile_edge(ts);
-            store_tile(0);
+        for (int u = 0; u < ntiles; ++u) {
+            const int ts = tstart(u);
+            const int buf = u & 1;
+            if (u >= nfull) {            // the sequence's last tile
+                load_tile_edge(ts);
+                store_tile(buf);
+            }
+            // this tile's gathers have landed (each wave waits for its own,
+            // the barrier for everyone's); all waves are done with buf ^ 1
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            if (active(ts)) {
-                qk(0, SA);
-                update_ref(mask_max(ts, SA));
-                probs(SA, pf);
-                pv(0, pf);
+            if (u + 1 < nfull) {
+                dma_k(tstart(u + 1), buf ^ 1);
+                dma_v(tstart(u + 1), buf ^ 1);
+            }
+            if (!active(ts)) continue;
+            const bool masked = (ts + kKeys - 1 > c + wt_min) || (ts + kKeys > k1);
+            if constexpr (kHandOrdered) {
+                compute_tile(buf, ts, masked);
+            } else {
+                qk(buf, S);
+                update_ref(mask_max(ts, S));
+                probs(S, pf);
+                pv(buf, pf);
             }
         }
     }

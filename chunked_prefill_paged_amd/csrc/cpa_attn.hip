@@ -279,21 +279,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
         for (int i = 0; i < NLD; ++i) {
             const int sl = wave * NLD + i;
             const int j0 = ts + sl * RK;
-            const uint32_t blk = min((uint32_t)bt[j0 >> lbs], nb_max);
-            const T* src = kc + (((size_t)blk * G + g) * bs + (j0 & (bs - 1))) * D + k_dma_off[i];
-            __builtin_amdgcn_global_load_lds((const void*)src, (void*)((char*)&lds_k[buf][0] + sl * 1024),
-                                             16, 0, 0);
+            const uint32_t blk = __builtin_amdgcn_readfirstlane(min((uint32_t)bt[j0 >> lbs], nb_max));
+            const char* base = (const char*)(kc + (((size_t)blk * G + g) * bs + (j0 & (bs - 1))) * D);
+            __builtin_amdgcn_global_load_lds((const void*)(base + (uint32_t)(k_dma_off[i] * (int)sizeof(T))),
+                                             (void*)((char*)&lds_k[buf][0] + sl * 1024), 16, 0, 0);
         }
     };
     auto dma_v = [&](int ts, int buf) {
+        if (bs >= kKeys) {
+            // the 64 keys of the tile share one block: scalar base, 32-bit lane offsets
+            const uint32_t blk = __builtin_amdgcn_readfirstlane(min((uint32_t)bt[ts >> lbs], nb_max));
+            const char* base = (const char*)(vc + ((size_t)blk * G + g) * D * bs + (ts & (bs - 1)));
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int sl = wave * NLD + i;
-            const int j = ts + v_dma_key(i);
-            const uint32_t blk = min((uint32_t)bt[j >> lbs], nb_max);
-            const T* src = vc + (((size_t)blk * G + g) * D + v_d0 + i * RV) * bs + (j & (bs - 1));
-            __builtin_amdgcn_global_load_lds((const void*)src, (void*)((char*)&lds_v[buf][0] + sl * 1024),
-                                             16, 0, 0);
+            for (int i = 0; i < NLD; ++i) {
+                const int sl = wave * NLD + i;
+                const uint32_t off = (uint32_t)(((v_d0 + i * RV) * bs + v_dma_key(i)) * (int)sizeof(T));
+                __builtin_amdgcn_global_load_lds((const void*)(base + off),
+                                                 (void*)((char*)&lds_v[buf][0] + sl * 1024), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                const int sl = wave * NLD + i;
+                const int j = ts + v_dma_key(i);
+                const uint32_t blk = min((uint32_t)bt[j >> lbs], nb_max);
+                const T* src = vc + (((size_t)blk * G + g) * D + v_d0 + i * RV) * bs + (j & (bs - 1));
+                __builtin_amdgcn_global_load_lds((const void*)src,
+                                                 (void*)((char*)&lds_v[buf][0] + sl * 1024), 16, 0, 0);
+            }
         }
     };
     auto store_tile = [&](int buf) {
@@ -511,7 +524,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                 fr[(f + 3) & 3] = frag(f + 3);
                 S1 = E::mma(fr[f & 3], qf[f & 7], S1);
                 const int r = 4 * (f - 8);
-                hm = fmaxf(hm, fmaxf(fmaxf(S0[r], S0[r + 1]), fmaxf(S0[r + 2], S0[r + 3])));
+                hm = fmaxf(hm, fmaxf(S0[r], S0[r + 1]));
+                hm = fmaxf(hm, fmaxf(S0[r + 2], S0[r + 3]));
                 __builtin_amdgcn_sched_barrier(0);
             }
             decide(hm);

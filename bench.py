@@ -16,10 +16,18 @@ wall time of the steps -> TFLOP/s, and as a fraction of the MI355X dense
 bf16 MFMA peak.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --copy-probe      # one plain 1 GiB device copy, for
+                                      # calibrating HBM byte counters
+
+The roofline's "traffic" is the attention kernel's HBM bytes per launch as
+measured by hardware counters and recorded, with the hash of the kernel
+sources it was measured on, in profiles/attn_kernel_10k_prompt_hbm_traffic.txt;
+it is reported only while those sources are unchanged (null otherwise).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +37,10 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("chunked_prefill_paged_amd/csrc/cpa_attn.hip", "chunked_prefill_paged_amd/csrc/cpa_plan.h")
+TRAFFIC_FILE = "profiles/attn_kernel_10k_prompt_hbm_traffic.txt"
+COPY_PROBE_BYTES = 1 << 30
 
 
 def _args():
@@ -40,7 +52,51 @@ def _args():
     ap.add_argument("--split-keys-prefill", type=int, default=0,
                     help="0 automatic, -1 never, else keys per work item")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy 5 times and exit")
     return ap.parse_args()
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when the kernel sources changed since it was measured."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith((" ", "#", "|")):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe():
+    """A plain device copy of known size: what HBM byte counters read for it
+    calibrates what they read for the attention kernel."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": COPY_PROBE_BYTES, "copy_probe_bytes_written":
+                      COPY_PROBE_BYTES, "launches": 5}), flush=True)
 
 
 class PromptBench:
@@ -144,9 +200,11 @@ class PromptBench:
         self.rid += 1
 
 
-def cpu_baseline(bench):
-    """The oracle as it stands, on a bounded sample of the same workload:
-    chunk 5 (1808 tokens over 8192 cached) for query heads 0-15."""
+def cpu_baseline(w, max_blocks):
+    """The oracle as it stands, timed over one whole step of the same
+    workload: the 10k prompt's five chunks, every query head, with the
+    oracle's scheduler, cache write and attention (NumPy float64)."""
+    import torch
     from threadpoolctl import threadpool_info
 
     from oracle import attention as oa
@@ -154,37 +212,33 @@ def cpu_baseline(bench):
     from oracle import schedule as osch
     from synth import free_block_order, prompt_qkv
 
-    w = bench.w
-    torch = bench.torch
     q32, k32, v32 = prompt_qkv(w)
-    q64 = torch.from_numpy(q32).to(torch.bfloat16).to(torch.float64).numpy()
-    k64 = torch.from_numpy(k32).to(torch.bfloat16).to(torch.float64).numpy()
-    v64 = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
-    pool = osch.BlockPool(w.num_blocks, free_block_order(w.num_blocks, w.seed))
-    sched = osch.Scheduler(pool, w.block_size, w.max_batched_tokens, bench.max_blocks)
-    sched.add_request(0, w.prompt_len)
+    q64, k64, v64 = (torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+                     for x in (q32, k32, v32))
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
     kp, vp = np.zeros(shape), np.zeros(shape)
-    heads = list(range(16))
-    pos, elapsed, flops = 0, 0.0, 0
-    for _ in bench.chunks:
+    t0 = time.perf_counter()
+    pool = osch.BlockPool(w.num_blocks, free_block_order(w.num_blocks, w.seed))
+    sched = osch.Scheduler(pool, w.block_size, w.max_batched_tokens, max_blocks)
+    sched.add_request(0, w.prompt_len)
+    pos, flops = 0, 0
+    while pos < w.prompt_len:
         b = sched.step()
         n = b["num_tokens"]
         kp, vp = oa.cache_write(kp, vp, k64[pos:pos + n], v64[pos:pos + n], b["block_table"],
                                 b["cu_seqlens_q"], b["cached_seq_len"], w.block_size)
-        if pos + n == w.prompt_len:          # the sampled chunk
-            t0 = time.perf_counter()
-            oa.attention(q64[pos:pos + n], kp, vp, b["block_table"], b["cu_seqlens_q"],
-                         b["cached_seq_len"], w.block_size, w.scale, w.num_kv_heads, heads=heads)
-            elapsed = time.perf_counter() - t0
-            flops = counters.attention_flops(counters.pairs(n, pos), len(heads), w.head_dim)
+        oa.attention(q64[pos:pos + n], kp, vp, b["block_table"], b["cu_seqlens_q"],
+                     b["cached_seq_len"], w.block_size, w.scale, w.num_kv_heads)
+        flops += counters.attention_flops(counters.pairs(n, pos), w.num_heads, w.head_dim)
         sched.commit()
         pos += n
+    elapsed = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": round(elapsed, 2),
-            "sample": "chunk 5 of the 10k prompt (1808 tokens over 8192 cached), query heads "
-                      "0-15 of 32, numpy float64"}
+            "sample": "one whole step: the 10k prompt's 5 chunks (2048x4 + 1808), all 32 query "
+                      "heads, oracle scheduler + cache write + attention in numpy float64 "
+                      f"({flops / 1e9:.2f} GFLOP)"}
 
 
 def main():
@@ -197,6 +251,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe()
+        return
     bench = PromptBench(args.kv_segment_size, args.split_keys_prefill)
     flops = bench.flops_per_step()
     for _ in range(args.warmup):
@@ -240,12 +297,12 @@ def main():
         "attention_ms_per_chunk": [round(x, 4) for x in per_chunk_ms],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": recorded_traffic(),
                      "kernel": "attn_kernel<bf16,128> (+ merge_kernel when rows are split)"},
         "plan": [{"items": p["num_items"], "merge_rows": p["num_merge_rows"]} for p in bench.plan],
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(bench)
+        line["cpu_baseline"] = cpu_baseline(bench.w, bench.max_blocks)
     print(json.dumps(line), flush=True)
 
 

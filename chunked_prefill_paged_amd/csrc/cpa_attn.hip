@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: slab indices stay scalar
     const int half = lane >> 5;
     const int lrow = lane & 31;
     const int G = p.num_kv_heads;
@@ -274,22 +274,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
         const int d = v_d0 + i * RV;
         return ((lane % NCV) ^ (((d & 7) ^ ((d >> 3) & 1)) & SWV)) * EPC;
     };
-    auto dma_k = [&](int ts, int buf) {
+    // Block ids of a tile's keys: lane L holds entry L of the (at most
+    // kKeys / 8) table entries the tile spans.  They are loaded one tile
+    // ahead, so issuing the gathers never waits on a table read.
+    const int nbt = bs >= kKeys ? 1 : (kKeys >> lbs);
+    auto load_bt = [&](int ts) -> int {
+        return (int)min((uint32_t)bt[(ts >> lbs) + min(lane, nbt - 1)], nb_max);
+    };
+    const char* kc_g = (const char*)(kc + (size_t)g * bs * D);
+    const char* vc_g = (const char*)(vc + (size_t)g * D * bs);
+    const uint32_t blk_bytes = (uint32_t)(G * bs * D * (int)sizeof(T));
+    auto dma_k = [&](int ts, int buf, int btv) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int sl = wave * NLD + i;
-            const int j0 = ts + sl * RK;
-            const uint32_t blk = __builtin_amdgcn_readfirstlane(min((uint32_t)bt[j0 >> lbs], nb_max));
-            const char* base = (const char*)(kc + (((size_t)blk * G + g) * bs + (j0 & (bs - 1))) * D);
-            __builtin_amdgcn_global_load_lds((const void*)(base + (uint32_t)(k_dma_off[i] * (int)sizeof(T))),
+            const int kt = sl * RK;                        // first key of the slab within the tile
+            const uint32_t blk = (uint32_t)__builtin_amdgcn_readlane(btv, bs >= kKeys ? 0 : (kt >> lbs));
+            const char* base = kc_g + (size_t)blk * blk_bytes;
+            const uint32_t off = (uint32_t)(((ts + kt) & (bs - 1)) * (D * (int)sizeof(T)))
+                               + (uint32_t)(k_dma_off[i] * (int)sizeof(T));
+            __builtin_amdgcn_global_load_lds((const void*)(base + off),
                                              (void*)((char*)&lds_k[buf][0] + sl * 1024), 16, 0, 0);
         }
     };
-    auto dma_v = [&](int ts, int buf) {
+    auto dma_v = [&](int ts, int buf, int btv) {
         if (bs >= kKeys) {
             // the 64 keys of the tile share one block: scalar base, 32-bit lane offsets
-            const uint32_t blk = __builtin_amdgcn_readfirstlane(min((uint32_t)bt[ts >> lbs], nb_max));
-            const char* base = (const char*)(vc + ((size_t)blk * G + g) * D * bs + (ts & (bs - 1)));
+            const uint32_t blk = (uint32_t)__builtin_amdgcn_readlane(btv, 0);
+            const char* base = vc_g + (size_t)blk * blk_bytes + (ts & (bs - 1)) * (int)sizeof(T);
 #pragma unroll
             for (int i = 0; i < NLD; ++i) {
                 const int sl = wave * NLD + i;
@@ -301,10 +313,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
 #pragma unroll
             for (int i = 0; i < NLD; ++i) {
                 const int sl = wave * NLD + i;
-                const int j = ts + v_dma_key(i);
-                const uint32_t blk = min((uint32_t)bt[j >> lbs], nb_max);
-                const T* src = vc + (((size_t)blk * G + g) * D + v_d0 + i * RV) * bs + (j & (bs - 1));
-                __builtin_amdgcn_global_load_lds((const void*)src,
+                const int kk = v_dma_key(i);                // key offset within the tile (per lane)
+                const uint32_t blk = (uint32_t)__shfl(btv, kk >> lbs);
+                const char* base = vc_g + (size_t)blk * blk_bytes;
+                const uint32_t off = (uint32_t)(((v_d0 + i * RV) * bs + ((ts + kk) & (bs - 1))) * (int)sizeof(T));
+                __builtin_amdgcn_global_load_lds((const void*)(base + off),
                                                  (void*)((char*)&lds_v[buf][0] + sl * 1024), 16, 0, 0);
             }
         }
@@ -584,10 +597,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
         Scores S;
         Frag pf[NKS];
         auto tstart = [&](int u) { return (tile0 + u) * kKeys; };
+        int btn = 0;                     // block ids of tile u + 1
         if (nfull > 0) {
-            dma_k(tstart(0), 0);
-            dma_v(tstart(0), 0);
+            const int bt0 = load_bt(tstart(0));
+            dma_k(tstart(0), 0, bt0);
+            dma_v(tstart(0), 0, bt0);
         }
+        if (nfull > 1) btn = load_bt(tstart(1));
         for (int u = 0; u < ntiles; ++u) {
             const int ts = tstart(u);
             const int buf = u & 1;
@@ -600,9 +616,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (u + 1 < nfull) {
-                dma_k(tstart(u + 1), buf ^ 1);
-                dma_v(tstart(u + 1), buf ^ 1);
+                dma_k(tstart(u + 1), buf ^ 1, btn);
+                dma_v(tstart(u + 1), buf ^ 1, btn);
             }
+            if (u + 2 < nfull) btn = load_bt(tstart(u + 2));
             if (!active(ts)) continue;
             const bool masked = (ts + kKeys - 1 > c + wt_min) || (ts + kKeys > k1);
             if constexpr (kHandOrdered) {

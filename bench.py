@@ -52,6 +52,9 @@ def _args():
     ap.add_argument("--split-keys-prefill", type=int, default=0,
                     help="0 automatic, -1 never, else keys per work item")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=("c2", "c4", "c5"), default="c2",
+                    help="c2: the 10k prompt (headline line); c5: the 32k prompt, per chunk "
+                         "and against one monolithic call; c4: the mixed decode + prefill batch")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device-to-device copy 5 times and exit")
     return ap.parse_args()
@@ -100,15 +103,16 @@ def copy_probe():
 
 
 class PromptBench:
-    """The 10k-token prompt, its device buffers and the per-chunk calls."""
+    """One chunked prompt (the 10k prompt by default), its device buffers and
+    the per-chunk calls."""
 
-    def __init__(self, kv_segment_size, split_pre):
+    def __init__(self, kv_segment_size, split_pre, workload="c2"):
         import torch
         from chunked_prefill_paged_amd import AttnCall, HostScheduler, cache_shapes
         from synth import free_block_order, get_workload, prompt_qkv
 
         self.torch = torch
-        w = get_workload("c2")
+        w = get_workload(workload)
         self.w = w
         q32, k32, v32 = prompt_qkv(w)
         dev = "cuda"
@@ -134,10 +138,15 @@ class PromptBench:
         pos = 0
         ws_bytes = 256
         for n in self.chunks:
-            d_i32 = torch.zeros(2 + 1 + self.max_blocks, dtype=torch.int32, device=dev)
-            d_i64 = torch.zeros(n, dtype=torch.int64, device=dev)
-            p_i32 = torch.zeros(d_i32.shape, dtype=torch.int32, pin_memory=True)
-            p_i64 = torch.zeros(d_i64.shape, dtype=torch.int64, pin_memory=True)
+            # one descriptor buffer per chunk (int32 cu_seqlens_q, cached_seq_len,
+            # block-table row; then the int64 slot mapping), uploaded with one copy
+            n32 = 2 + 1 + self.max_blocks
+            off64 = -(-4 * n32 // 8) * 8
+            nbytes = off64 + 8 * n
+            d_all = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+            p_all = torch.zeros(nbytes, dtype=torch.uint8, pin_memory=True)
+            d_i32, d_i64 = d_all[:4 * n32].view(torch.int32), d_all[off64:].view(torch.int64)
+            p_i32, p_i64 = p_all[:4 * n32].view(torch.int32), p_all[off64:].view(torch.int64)
             call = AttnCall(q=self.q[pos:pos + n], k_new=self.k[pos:pos + n], v_new=self.v[pos:pos + n],
                             k_cache=self.k_cache, v_cache=self.v_cache, out=self.out[pos:pos + n],
                             cu_seqlens_q=d_i32[0:2], cached_seq_len=d_i32[2:3],
@@ -147,8 +156,8 @@ class PromptBench:
                             kv_segment_size=kv_segment_size, split_keys_prefill=split_pre)
             ws_bytes = max(ws_bytes, call.workspace_bytes())
             self.calls.append(call)
-            self.dev_desc.append((d_i32, d_i64))
-            self.pinned.append((p_i32, p_i64))
+            self.dev_desc.append((d_all, d_i32, d_i64))
+            self.pinned.append((p_all, p_i32, p_i64))
             self.copied.append(None)
             pos += n
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -172,7 +181,7 @@ class PromptBench:
         sched.add_request(self.rid, self.w.prompt_len)
         for i, call in enumerate(self.calls):
             b = sched.step()
-            p_i32, p_i64 = self.pinned[i]
+            p_all, p_i32, p_i64 = self.pinned[i]
             if self.copied[i] is not None:
                 self.copied[i].synchronize()        # staging buffer of the previous step is free
             a32 = p_i32.numpy()
@@ -180,9 +189,7 @@ class PromptBench:
             a32[2] = b["cached_seq_len"][0]
             a32[3:] = b["block_table"][0]
             p_i64.numpy()[:] = b["slot_mapping"]
-            d_i32, d_i64 = self.dev_desc[i]
-            d_i32.copy_(p_i32, non_blocking=True)
-            d_i64.copy_(p_i64, non_blocking=True)
+            self.dev_desc[i][0].copy_(p_all, non_blocking=True)
             ev = torch.cuda.Event()
             ev.record()
             self.copied[i] = ev
@@ -243,6 +250,171 @@ def cpu_baseline(w, max_blocks):
                       f"({flops / 1e9:.2f} GFLOP)"}
 
 
+def _time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def run_long_prompt(args):
+    """The 32,768-token prompt (GQA 64/8, bs16, S4096) in 16 chunks of 2048:
+    TFLOP/s of every chunk as the cached length grows, and the whole chunked
+    prompt against one monolithic causal call over all 32k tokens."""
+    import torch
+    S = 4096 if args.kv_segment_size == 1024 else args.kv_segment_size
+    bench = PromptBench(S, args.split_keys_prefill, workload="c5")
+    w = bench.w
+    steps = max(1, min(args.steps, 5))
+    warm = max(1, min(args.warmup, 2))
+    for _ in range(warm):
+        bench.step()
+    torch.cuda.synchronize()
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in bench.chunks] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for st in range(steps):
+        bench.step([list(p) for p in events[st]])
+    torch.cuda.synchronize()
+    chunked_s = (time.perf_counter() - t0) / steps
+    per_chunk_ms = [sum(events[st][i][0].elapsed_time(events[st][i][1]) for st in range(steps)) / steps
+                    for i in range(len(bench.chunks))]
+    H, D, c, per_chunk_tf = w.num_heads, w.head_dim, 0, []
+    for n, ms in zip(bench.chunks, per_chunk_ms):
+        per_chunk_tf.append(round(4 * H * D * (n * c + n * (n + 1) // 2) / (ms / 1e3) / 1e12, 1))
+        c += n
+    # monolithic: one call over the whole prompt, nothing cached (same slots)
+    from chunked_prefill_paged_amd import AttnCall
+    from synth import free_block_order
+    P = w.prompt_len
+    # the whole pool (exactly the prompt's 2048 blocks) in its seeded order
+    table = np.ascontiguousarray(free_block_order(w.num_blocks, w.seed)[:P // w.block_size])
+    dev = "cuda"
+    cu = torch.tensor([0, P], dtype=torch.int32, device=dev)
+    cached = torch.zeros(1, dtype=torch.int32, device=dev)
+    bt = torch.from_numpy(table).view(1, -1).to(dev)
+    slots = (torch.from_numpy(table.astype(np.int64)).to(dev).repeat_interleave(w.block_size)
+             * w.block_size + torch.arange(P, device=dev) % w.block_size)
+    mono = AttnCall(q=bench.q, k_new=bench.k, v_new=bench.v, k_cache=bench.k_cache,
+                    v_cache=bench.v_cache, out=bench.out, cu_seqlens_q=cu, cached_seq_len=cached,
+                    block_table=bt, slot_mapping=slots, h_cu_seqlens_q=np.array([0, P], np.int32),
+                    h_cached_seq_len=np.array([0], np.int32), kv_segment_size=S,
+                    split_keys_prefill=args.split_keys_prefill)
+    ws = torch.empty(mono.workspace_bytes(), dtype=torch.uint8, device=dev)
+    mono.set_workspace(ws)
+    mono_s = _time_steps(torch, mono, steps, warm)
+    flops = bench.flops_per_step()
+    print(json.dumps({
+        "metric": "32k-prompt chunked prefill TFLOP/s per chunk; chunked vs monolithic time",
+        "value": round(flops / chunked_s / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(chunked_s * 1e3, 3),
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "32,768-token prompt in 16 chunks of 2048 (cached 0..30720), "
+                               f"H64/G8/D128, block_size 16, kv_segment_size {S}"},
+        "gflop_per_step": round(flops / 1e9, 2),
+        "attention_ms_per_chunk": [round(x, 4) for x in per_chunk_ms],
+        "attention_tflops_per_chunk": per_chunk_tf,
+        "monolithic_ms": round(mono_s * 1e3, 3),
+        "monolithic_tflops": round(flops / mono_s / 1e12, 2),
+        "chunked_over_monolithic": round(chunked_s / mono_s, 4),
+    }), flush=True)
+
+
+def run_mixed_batch(args):
+    """The piggybacked batch: 256 decodes (context 16*U{64..2048}) plus a
+    1792-token chunk of a 32k prompt at cached 30,720, one varlen call under
+    a 2048-token budget (bs16, S2048, GQA 32/8).  Times the mixed call, the
+    decode rows alone (achieved HBM GB/s over the KV they read) and the
+    prefill rows alone (TFLOP/s)."""
+    import math
+
+    import torch
+    from chunked_prefill_paged_amd import AttnCall, HostScheduler, cache_shapes
+    from synth import config4_decode_contexts, free_block_order, get_workload
+
+    w = get_workload("c4")
+    H, G, D, bs = w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
+    S = 2048 if args.kv_segment_size == 1024 else args.kv_segment_size
+    ctx = [int(x) for x in config4_decode_contexts(w)]
+    pf_cached, pf_prompt = 30720, w.prompt_len
+    demand = sum(-(-(L + 1) // bs) for L in ctx) + -(-(pf_cached + 1792) // bs)
+    nb = math.ceil(1.2 * demand)
+    max_blocks = -(-(max(ctx) + 1) // bs) + 1
+    sched = HostScheduler(nb, bs, w.max_batched_tokens, max(max_blocks, pf_prompt // bs),
+                          free_order=free_block_order(nb, w.seed))
+    for i, L in enumerate(ctx):
+        sched.add_decode(i, L)
+    sched.add_partial(256, pf_prompt, pf_cached)
+    b = sched.step()
+    T = int(b["num_tokens"])
+    dev = "cuda"
+    ks, vs = cache_shapes(nb, G, bs, D)
+    k_cache = torch.empty(ks, dtype=torch.bfloat16, device=dev)
+    v_cache = torch.empty(vs, dtype=torch.bfloat16, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    for t in (k_cache, v_cache):             # the cached context: seeded N(0,1)
+        for i in range(0, nb, 8192):
+            t[i:i + 8192].normal_(generator=gen)
+    q = torch.randn((T, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    kn = torch.randn((T, G, D), generator=gen, device=dev).to(torch.bfloat16)
+    vn = torch.randn((T, G, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    cu_h = np.ascontiguousarray(b["cu_seqlens_q"], dtype=np.int32)
+    cached_h = np.ascontiguousarray(b["cached_seq_len"], dtype=np.int32)
+    table_h = np.ascontiguousarray(b["block_table"], dtype=np.int32)
+    slots_h = np.ascontiguousarray(b["slot_mapping"], dtype=np.int64)
+    d = lambda a: torch.from_numpy(a).to(dev)
+    cu, cached, table, slots = d(cu_h), d(cached_h), d(table_h), d(slots_h)
+
+    def make(seqs):
+        lo, hi = seqs
+        t0, t1 = int(cu_h[lo]), int(cu_h[hi])
+        call = AttnCall(q=q[t0:t1], k_new=kn[t0:t1], v_new=vn[t0:t1], k_cache=k_cache,
+                        v_cache=v_cache, out=out[t0:t1],
+                        cu_seqlens_q=(cu[lo:hi + 1] - t0).contiguous(),
+                        cached_seq_len=cached[lo:hi].contiguous(),
+                        block_table=table[lo:hi].contiguous(), slot_mapping=slots[t0:t1].contiguous(),
+                        h_cu_seqlens_q=cu_h[lo:hi + 1] - t0, h_cached_seq_len=cached_h[lo:hi],
+                        kv_segment_size=S, split_keys_prefill=args.split_keys_prefill)
+        call.set_workspace(torch.empty(call.workspace_bytes(), dtype=torch.uint8, device=dev))
+        return call
+
+    B = len(cu_h) - 1
+    mixed, decodes, prefill = make((0, B)), make((0, B - 1)), make((B - 1, B))
+    steps, warm = max(1, args.steps), max(1, args.warmup)
+    t_mixed = _time_steps(torch, mixed, steps, warm)
+    t_dec = _time_steps(torch, decodes, steps, warm)
+    t_pre = _time_steps(torch, prefill, steps, warm)
+    dec_bytes = sum(2 * (L + 1) * G * D * 2 for L in ctx)          # K and V each decode reads
+    n_pre = T - 256
+    pre_flops = 4 * H * D * (n_pre * pf_cached + n_pre * (n_pre + 1) // 2)
+    dec_flops = sum(4 * H * D * (L + 1) for L in ctx)
+    print(json.dumps({
+        "metric": "mixed decode + prefill batch: decode GB/s, prefill TFLOP/s, mixed call time",
+        "value": round(dec_bytes / t_dec / 1e9, 1), "unit": "GB/s (decode rows)", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(t_mixed * 1e3, 4),
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"256 decodes (context 16*U{{64..2048}}) + 1792-token chunk at "
+                               f"cached 30720, budget 2048, bs16, S{S}, H32/G8/D128, "
+                               f"pool {nb} blocks ({2 * nb * G * bs * D * 2 / 1e9:.1f} GB K+V)"},
+        "mixed_ms": round(t_mixed * 1e3, 4),
+        "decode_only_ms": round(t_dec * 1e3, 4),
+        "decode_kv_gb": round(dec_bytes / 1e9, 3),
+        "decode_gbps": round(dec_bytes / t_dec / 1e9, 1),
+        "decode_frac_of_hbm_peak": round(dec_bytes / t_dec / 1e9 / PEAK_HBM_GBS, 4),
+        "prefill_only_ms": round(t_pre * 1e3, 4),
+        "prefill_tflops": round(pre_flops / t_pre / 1e12, 1),
+        "mixed_tflops": round((pre_flops + dec_flops) / t_mixed / 1e12, 1),
+        "roofline_mixed_ms": round(max(dec_bytes / (PEAK_HBM_GBS * 1e9),
+                                       (pre_flops + dec_flops) / (PEAK_BF16_TFLOPS * 1e12)) * 1e3, 4),
+    }), flush=True)
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -255,6 +427,12 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.workload == "c5":
+        run_long_prompt(args)
+        return
+    if args.workload == "c4":
+        run_mixed_batch(args)
         return
     bench = PromptBench(args.kv_segment_size, args.split_keys_prefill)
     flops = bench.flops_per_step()

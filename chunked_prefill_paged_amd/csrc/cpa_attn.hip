@@ -766,7 +766,7 @@ struct PrepParams {
     int32_t* header;
 };
 
-constexpr int kPrepSmem = 2 * (kMaxSeqs + 1) * 4 > 64 * (128 + 1) * 4 ? 2 * (kMaxSeqs + 1) * 4
+constexpr int kPrepSmem = (3 * kMaxSeqs + 2) * 4 > 64 * (128 + 1) * 4 ? (3 * kMaxSeqs + 2) * 4
                                                                         : 64 * (128 + 1) * 4;
 
 // Rows of 64 new tokens of KV head g go to their slots.  K rows are copied
@@ -819,76 +819,110 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
     }
 }
 
+// Inclusive scan of one value per thread over the workgroup (log-step).
+template <typename V>
+__device__ V block_scan_incl(V x, V* buf) {
+    const int tid = threadIdx.x;
+    buf[tid] = x;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+        const V y = tid >= off ? buf[tid - off] : V(0);
+        __syncthreads();
+        buf[tid] += y;
+        __syncthreads();
+    }
+    const V r = buf[tid];
+    __syncthreads();
+    return r;
+}
+
+// Work plan.  Items of prefill sequences (n > decode threshold) come first,
+// in sequence order, each sequence's longest row tiles first; items of
+// decode rows follow.  Long causal items thus start before the short ones,
+// and in a mixed batch the matrix-bound prefill items run while the
+// bandwidth-bound decode items fill the remaining slots.
 __device__ void build_plan(const PrepParams& p, char* smem) {
-    int* s_item = (int*)smem;                 // [kMaxSeqs + 1]
-    int* s_merge = s_item + (kMaxSeqs + 1);   // [kMaxSeqs + 1]
-    __shared__ long long sc_items[kThreads];
-    __shared__ long long sc_parts[kThreads];
-    __shared__ int sc_merge[kThreads];
+    int* s_item = (int*)smem;                 // [kMaxSeqs + 1] first item of the k-th issued sequence
+    int* s_seq = s_item + (kMaxSeqs + 1);     // [kMaxSeqs]     sequence issued k-th
+    int* s_merge = s_seq + kMaxSeqs;          // [kMaxSeqs + 1] first merge row of sequence b
+    __shared__ long long sc_ll[kThreads];
+    __shared__ int sc_i[kThreads];
     const int B = p.num_seqs, tid = threadIdx.x;
     const int per = (B + kThreads - 1) / kThreads;
     const int b_lo = min(B, tid * per), b_hi = min(B, b_lo + per);
-    long long items = 0, parts = 0;
-    int merge = 0;
+    auto plan_of = [&](int b) {
+        return seq_plan(p.cu[b + 1] - p.cu[b], p.cached[b], p.hpg, p.num_heads, p.dec_thresh,
+                        p.split_pre, p.split_dec);
+    };
+    auto is_prefill = [&](int b) { return p.cu[b + 1] - p.cu[b] > p.dec_thresh; };
+    long long it_pre = 0, it_dec = 0, parts = 0;
+    int merge = 0, n_pre = 0;
     for (int b = b_lo; b < b_hi; ++b) {
-        const int n = p.cu[b + 1] - p.cu[b];
-        const SeqPlan sp = seq_plan(n, p.cached[b], p.hpg, p.num_heads, p.dec_thresh, p.split_pre,
-                                    p.split_dec);
-        items += sp.items;
+        const SeqPlan sp = plan_of(b);
+        if (is_prefill(b)) {
+            it_pre += sp.items;
+            ++n_pre;
+        } else {
+            it_dec += sp.items;
+        }
         parts += sp.parts;
         merge += sp.merge;
     }
-    sc_items[tid] = items;
-    sc_parts[tid] = parts;
-    sc_merge[tid] = merge;
-    __syncthreads();
-    if (tid == 0) {   // exclusive scan over the 256 thread sums
-        long long ai = 0, ap = 0;
-        int am = 0;
-        for (int i = 0; i < kThreads; ++i) {
-            const long long xi = sc_items[i], xp = sc_parts[i];
-            const int xm = sc_merge[i];
-            sc_items[i] = ai;
-            sc_parts[i] = ap;
-            sc_merge[i] = am;
-            ai += xi;
-            ap += xp;
-            am += xm;
-        }
-        s_item[B] = (int)ai;
-        s_merge[B] = am;
-        p.header[0] = (int)ai;
-        p.header[1] = am;
-        p.header[2] = (int)ap;
+    const long long sc_pre = block_scan_incl(it_pre, sc_ll);
+    const long long sc_dec = block_scan_incl(it_dec, sc_ll);
+    const long long sc_parts = block_scan_incl(parts, sc_ll);
+    const int sc_merge = block_scan_incl(merge, sc_i);
+    const int sc_npre = block_scan_incl(n_pre, sc_i);
+    __shared__ long long tot[3];
+    __shared__ int tot_i[2];
+    if (tid == kThreads - 1) {
+        tot[0] = sc_pre;
+        tot[1] = sc_dec;
+        tot[2] = sc_parts;
+        tot_i[0] = sc_merge;
+        tot_i[1] = sc_npre;
     }
     __syncthreads();
-    long long io = sc_items[tid], po = sc_parts[tid];
-    int mo = sc_merge[tid];
+    const long long items_pre = tot[0], items_all = tot[0] + tot[1];
+    const int npre_all = tot_i[1];
+    if (tid == 0) {
+        s_item[B] = (int)items_all;
+        s_merge[B] = tot_i[0];
+        p.header[0] = (int)items_all;
+        p.header[1] = tot_i[0];
+        p.header[2] = (int)tot[2];
+    }
+    // exclusive prefixes of this thread's range
+    long long io_pre = sc_pre - it_pre, io_dec = items_pre + sc_dec - it_dec, po = sc_parts - parts;
+    int mo = sc_merge - merge;
+    int k_pre = sc_npre - n_pre;                          // issue slot of the next prefill sequence
+    int k_dec = npre_all + (b_lo - (sc_npre - n_pre));    // decode sequences before b_lo: b_lo - prefill ones
     for (int b = b_lo; b < b_hi; ++b) {
-        const int n = p.cu[b + 1] - p.cu[b];
-        const SeqPlan sp = seq_plan(n, p.cached[b], p.hpg, p.num_heads, p.dec_thresh, p.split_pre,
-                                    p.split_dec);
+        const SeqPlan sp = plan_of(b);
+        const bool pre = is_prefill(b);
+        const long long io = pre ? io_pre : io_dec;
+        const int k = pre ? k_pre++ : k_dec++;
         p.seq_info[b] = make_int4((int)io, sp.nsplit, (int)po, mo);
-        s_item[b] = (int)io;
+        s_item[k] = (int)io;
+        s_seq[k] = b;
         s_merge[b] = mo;
-        io += sp.items;
+        if (pre) io_pre += sp.items; else io_dec += sp.items;
         po += sp.parts;
         mo += sp.merge;
     }
     __syncthreads();
     const int total_items = s_item[B];
     for (int i = tid; i < total_items; i += kThreads) {
-        int lo = 0, hi = B;   // s_item[lo] <= i < s_item[hi]
+        int lo = 0, hi = B;   // s_item[lo] <= i < s_item[hi] (issue order)
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (s_item[mid] <= i) lo = mid; else hi = mid;
         }
-        const int n = p.cu[lo + 1] - p.cu[lo];
-        const SeqPlan sp = seq_plan(n, p.cached[lo], p.hpg, p.num_heads, p.dec_thresh, p.split_pre,
-                                    p.split_dec);
+        const int bq = s_seq[lo];
+        const SeqPlan sp = plan_of(bq);
         const int local = i - s_item[lo];
         const int rt = sp.tiles - 1 - local / sp.nsplit;   // longest row tiles first
-        p.items[i] = make_int4(lo, rt, local % sp.nsplit, sp.nsplit);
+        p.items[i] = make_int4(bq, rt, local % sp.nsplit, sp.nsplit);
     }
     const int total_merge = s_merge[B];
     for (int i = tid; i < total_merge; i += kThreads) {

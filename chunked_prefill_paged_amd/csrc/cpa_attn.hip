@@ -691,47 +691,52 @@ struct MergeParams {
     float* lse;
     int32_t num_heads;
     int32_t total_q;
+    int32_t num_merge;
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeParams p) {
-    const int2 e = p.merge[blockIdx.x];
+    // one thread per (merge row, head, 4-element chunk of D)
+    constexpr int NC = D / 4;
+    const int H = p.num_heads;
+    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (gid >= (int64_t)p.num_merge * H * NC) return;
+    const int row = (int)(gid / (H * NC));
+    const int h = (int)(gid / NC % H), dc = (int)(gid % NC);
+    const int2 e = p.merge[row];
     const int b = e.x, t = e.y;
     const int q0 = p.cu[b];
     const int n = p.cu[b + 1] - q0;
     const int4 si = p.seq_info[b];
     const int nsplit = si.y;
-    const size_t base = (size_t)si.z;
-    const int H = p.num_heads;
-    constexpr int NC = D / 4;
-    for (int idx = threadIdx.x; idx < H * NC; idx += kThreads) {
-        const int h = idx / NC, dc = idx % NC;
-        float m = -INFINITY;
-        for (int s = 0; s < nsplit; ++s)
-            m = fmaxf(m, p.part_ml[base + ((size_t)s * n + t) * H + h].x);
-        float l = 0.f;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < nsplit; ++s) {
-            const size_t pi = base + ((size_t)s * n + t) * H + h;
-            const float2 ml = p.part_ml[pi];
-            if (ml.x == -INFINITY) continue;
-            const float w = __builtin_amdgcn_exp2f(ml.x - m);
-            l += w * ml.y;
-            acc += w * *(const f32x4*)(p.part_o + pi * D + dc * 4);
-        }
-        const float inv = 1.f / l;
-        T* op = (T*)p.out + ((size_t)(q0 + t) * H + h) * D + dc * 4;
-        if constexpr (sizeof(T) == 2) {
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            bf16x4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[i] * inv);
-            *(bf16x4*)op = v;
-        } else {
-            *(f32x4*)op = acc * inv;
-        }
-        if (p.lse && dc == 0) p.lse[(size_t)h * p.total_q + q0 + t] = (m + __log2f(l)) * kLn2;
+    const size_t base = (size_t)si.z + (size_t)t * H + h;   // partial of split s at base + s*n*H
+    const size_t sstride = (size_t)n * H;
+    float m = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, p.part_ml[base + s * sstride].x);
+    float l = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int s = 0; s < nsplit; ++s) {
+        const size_t pi = base + s * sstride;
+        const float2 ml = p.part_ml[pi];
+        const f32x4 o = *(const f32x4*)(p.part_o + pi * D + dc * 4);
+        // a split with no visible key has m = -inf, l = 0 and O = 0
+        const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - m);
+        l += w * ml.y;
+        acc += w * o;
     }
+    const float inv = 1.f / l;
+    T* op = (T*)p.out + ((size_t)(q0 + t) * H + h) * D + dc * 4;
+    if constexpr (sizeof(T) == 2) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[i] * inv);
+        *(bf16x4*)op = v;
+    } else {
+        *(f32x4*)op = acc * inv;
+    }
+    if (p.lse && dc == 0) p.lse[(size_t)h * p.total_q + q0 + t] = (m + __log2f(l)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -911,27 +916,22 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
         mo += sp.merge;
     }
     __syncthreads();
-    const int total_items = s_item[B];
-    for (int i = tid; i < total_items; i += kThreads) {
-        int lo = 0, hi = B;   // s_item[lo] <= i < s_item[hi] (issue order)
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_item[mid] <= i) lo = mid; else hi = mid;
-        }
-        const int bq = s_seq[lo];
+    // items and merge rows, one wave per sequence at a time (lanes over the
+    // sequence's items)
+    const int wv = tid >> 6, ln = tid & 63;
+    constexpr int kWaves = kThreads / 64;
+    for (int k = wv; k < B; k += kWaves) {        // k-th issued sequence
+        const int bq = s_seq[k];
+        const int i0 = s_item[k];
         const SeqPlan sp = plan_of(bq);
-        const int local = i - s_item[lo];
-        const int rt = sp.tiles - 1 - local / sp.nsplit;   // longest row tiles first
-        p.items[i] = make_int4(bq, rt, local % sp.nsplit, sp.nsplit);
-    }
-    const int total_merge = s_merge[B];
-    for (int i = tid; i < total_merge; i += kThreads) {
-        int lo = 0, hi = B;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_merge[mid] <= i) lo = mid; else hi = mid;
+        for (int local = ln; local < sp.items; local += 64) {
+            const int rt = sp.tiles - 1 - local / sp.nsplit;   // longest row tiles first
+            p.items[i0 + local] = make_int4(bq, rt, local % sp.nsplit, sp.nsplit);
         }
-        p.merge[i] = make_int2(lo, i - s_merge[lo]);
+    }
+    for (int b = wv; b < B; b += kWaves) {
+        const int m0 = s_merge[b], m1 = s_merge[b + 1];
+        for (int i = m0 + ln; i < m1; i += 64) p.merge[i] = make_int2(b, i - m0);
     }
 }
 
@@ -1115,7 +1115,10 @@ cpa_status launch_attention(const cpa_attn_args* a, const Resolved* r, hipStream
         m.lse = a->lse;
         m.num_heads = a->num_heads;
         m.total_q = a->total_q;
-        hipLaunchKernelGGL((merge_kernel<T, D>), dim3((int)r->merge), dim3(kThreads), 0, stream, m);
+        m.num_merge = (int32_t)r->merge;
+        const int64_t threads = r->merge * a->num_heads * (D / 4);
+        hipLaunchKernelGGL((merge_kernel<T, D>), dim3((int)((threads + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, stream, m);
         if (hipGetLastError() != hipSuccess) return CPA_ERR_HIP;
     }
     return CPA_OK;

@@ -771,8 +771,9 @@ struct PrepParams {
     int32_t* header;
 };
 
-constexpr int kPrepSmem = (3 * kMaxSeqs + 2) * 4 > 64 * (128 + 1) * 4 ? (3 * kMaxSeqs + 2) * 4
-                                                                        : 64 * (128 + 1) * 4;
+constexpr int kPlanSmem = (3 * kMaxSeqs + 2) * 4 + kMaxSeqs * 2;
+constexpr int kPrepSmem = kPlanSmem > 64 * (128 + 1) * 4 ? kPlanSmem : 64 * (128 + 1) * 4;
+static_assert(kMaxSeqs <= 65536, "sequence ids are held as 16-bit values in the plan builder");
 
 // Rows of 64 new tokens of KV head g go to their slots.  K rows are copied
 // with 16-byte stores; V is staged in LDS and written as columns of the
@@ -848,8 +849,9 @@ __device__ V block_scan_incl(V x, V* buf) {
 // bandwidth-bound decode items fill the remaining slots.
 __device__ void build_plan(const PrepParams& p, char* smem) {
     int* s_item = (int*)smem;                 // [kMaxSeqs + 1] first item of the k-th issued sequence
-    int* s_seq = s_item + (kMaxSeqs + 1);     // [kMaxSeqs]     sequence issued k-th
-    int* s_merge = s_seq + kMaxSeqs;          // [kMaxSeqs + 1] first merge row of sequence b
+    int* s_merge = s_item + (kMaxSeqs + 1);   // [kMaxSeqs + 1] first merge row of sequence b
+    int* s_nsplit = s_merge + (kMaxSeqs + 1); // [kMaxSeqs]     splits of the k-th issued sequence
+    uint16_t* s_seq = (uint16_t*)(s_nsplit + kMaxSeqs);   // [kMaxSeqs] sequence issued k-th
     __shared__ long long sc_ll[kThreads];
     __shared__ int sc_i[kThreads];
     const int B = p.num_seqs, tid = threadIdx.x;
@@ -909,7 +911,8 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
         const int k = pre ? k_pre++ : k_dec++;
         p.seq_info[b] = make_int4((int)io, sp.nsplit, (int)po, mo);
         s_item[k] = (int)io;
-        s_seq[k] = b;
+        s_seq[k] = (uint16_t)b;
+        s_nsplit[k] = sp.nsplit;
         s_merge[b] = mo;
         if (pre) io_pre += sp.items; else io_dec += sp.items;
         po += sp.parts;
@@ -920,13 +923,15 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
     // sequence's items)
     const int wv = tid >> 6, ln = tid & 63;
     constexpr int kWaves = kThreads / 64;
+    // (issued sequences own contiguous item ranges: prefill ones, then decode ones)
     for (int k = wv; k < B; k += kWaves) {        // k-th issued sequence
         const int bq = s_seq[k];
-        const int i0 = s_item[k];
-        const SeqPlan sp = plan_of(bq);
-        for (int local = ln; local < sp.items; local += 64) {
-            const int rt = sp.tiles - 1 - local / sp.nsplit;   // longest row tiles first
-            p.items[i0 + local] = make_int4(bq, rt, local % sp.nsplit, sp.nsplit);
+        const int i0 = s_item[k], ni = s_item[k + 1] - i0;
+        const int nsplit = s_nsplit[k];
+        const int tiles = ni / nsplit;
+        for (int local = ln; local < ni; local += 64) {
+            const int rt = tiles - 1 - local / nsplit;   // longest row tiles first
+            p.items[i0 + local] = make_int4(bq, rt, local % nsplit, nsplit);
         }
     }
     for (int b = wv; b < B; b += kWaves) {

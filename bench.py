@@ -138,26 +138,23 @@ class PromptBench:
         pos = 0
         ws_bytes = 256
         for n in self.chunks:
-            # one descriptor buffer per chunk (int32 cu_seqlens_q, cached_seq_len,
-            # block-table row; then the int64 slot mapping), uploaded with one copy
+            # one int32 descriptor per chunk (cu_seqlens_q, cached_seq_len,
+            # block-table row), uploaded with one copy; no slot mapping: the
+            # library derives the slots from the block table
             n32 = 2 + 1 + self.max_blocks
-            off64 = -(-4 * n32 // 8) * 8
-            nbytes = off64 + 8 * n
-            d_all = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
-            p_all = torch.zeros(nbytes, dtype=torch.uint8, pin_memory=True)
-            d_i32, d_i64 = d_all[:4 * n32].view(torch.int32), d_all[off64:].view(torch.int64)
-            p_i32, p_i64 = p_all[:4 * n32].view(torch.int32), p_all[off64:].view(torch.int64)
+            d_i32 = torch.zeros(n32, dtype=torch.int32, device=dev)
+            p_i32 = torch.zeros(n32, dtype=torch.int32, pin_memory=True)
             call = AttnCall(q=self.q[pos:pos + n], k_new=self.k[pos:pos + n], v_new=self.v[pos:pos + n],
                             k_cache=self.k_cache, v_cache=self.v_cache, out=self.out[pos:pos + n],
                             cu_seqlens_q=d_i32[0:2], cached_seq_len=d_i32[2:3],
-                            block_table=d_i32[3:].view(1, self.max_blocks), slot_mapping=d_i64,
+                            block_table=d_i32[3:].view(1, self.max_blocks), slot_mapping=None,
                             h_cu_seqlens_q=np.array([0, n], np.int32),
                             h_cached_seq_len=np.array([pos], np.int32),
                             kv_segment_size=kv_segment_size, split_keys_prefill=split_pre)
             ws_bytes = max(ws_bytes, call.workspace_bytes())
             self.calls.append(call)
-            self.dev_desc.append((d_all, d_i32, d_i64))
-            self.pinned.append((p_all, p_i32, p_i64))
+            self.dev_desc.append(d_i32)
+            self.pinned.append(p_i32)
             self.copied.append(None)
             pos += n
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -181,15 +178,14 @@ class PromptBench:
         sched.add_request(self.rid, self.w.prompt_len)
         for i, call in enumerate(self.calls):
             b = sched.step()
-            p_all, p_i32, p_i64 = self.pinned[i]
+            p_i32 = self.pinned[i]
             if self.copied[i] is not None:
                 self.copied[i].synchronize()        # staging buffer of the previous step is free
             a32 = p_i32.numpy()
             a32[0:2] = b["cu_seqlens_q"]
             a32[2] = b["cached_seq_len"][0]
             a32[3:] = b["block_table"][0]
-            p_i64.numpy()[:] = b["slot_mapping"]
-            self.dev_desc[i][0].copy_(p_all, non_blocking=True)
+            self.dev_desc[i].copy_(p_i32, non_blocking=True)
             ev = torch.cuda.Event()
             ev.record()
             self.copied[i] = ev

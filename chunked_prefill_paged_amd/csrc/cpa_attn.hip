@@ -748,7 +748,9 @@ struct PrepParams {
     const void* v_new;
     void* k_cache;
     void* v_cache;
-    const int64_t* slots;
+    const int64_t* slots;             // NULL: derived from block_table
+    const int32_t* block_table;
+    int32_t max_blocks;
     int32_t total_q;
     int32_t num_kv_heads;
     int32_t block_size;
@@ -795,6 +797,30 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
     T* vc = (T*)p.v_cache;
     const int bs = p.block_size;
     const int64_t nslots = (int64_t)p.num_blocks * bs;
+    // slots of the 64 tokens: given, or derived from the block table (the
+    // token's sequence b by binary search over cu_seqlens_q, position
+    // cached_seq_len[b] + offset in its chunk)
+    __shared__ int64_t s_slot[64];
+    if (tid < ntok) {
+        const int tok = tok0 + tid;
+        int64_t slot;
+        if (p.slots) {
+            slot = p.slots[tok];
+        } else {
+            int lo = 0, hi = p.num_seqs;          // cu[lo] <= tok < cu[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (p.cu[mid] <= tok) lo = mid; else hi = mid;
+            }
+            const int pos = p.cached[lo] + (tok - p.cu[lo]);
+            const int col = pos >> p.log2_bs;
+            slot = col < p.max_blocks
+                       ? (int64_t)p.block_table[(size_t)lo * p.max_blocks + col] * bs + (pos & (bs - 1))
+                       : -1;
+        }
+        s_slot[tid] = slot;
+    }
+    __syncthreads();
     for (int cidx = tid; cidx < ntok * NCK; cidx += kThreads) {
         const int tk = cidx / NCK, ch = cidx - (cidx / NCK) * NCK;
         const size_t src = ((size_t)(tok0 + tk) * G + g) * D + ch * EPC;
@@ -805,7 +831,7 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
         dst[1] = vv.y;
         dst[2] = vv.z;
         dst[3] = vv.w;
-        const int64_t slot = p.slots[tok0 + tk];
+        const int64_t slot = s_slot[tk];
         if (slot >= 0 && slot < nslots) {
             const int64_t blk = slot >> p.log2_bs;
             const int off = (int)(slot & (bs - 1));
@@ -815,7 +841,7 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
     __syncthreads();
     const int lane = tid & 63, wave = tid >> 6;
     if (lane < ntok) {
-        const int64_t slot = p.slots[tok0 + lane];
+        const int64_t slot = s_slot[lane];
         if (slot >= 0 && slot < nslots) {
             const int64_t blk = slot >> p.log2_bs;
             const int off = (int)(slot & (bs - 1));
@@ -1030,7 +1056,12 @@ cpa_status resolve(const cpa_attn_args* a, Resolved* r) {
 }
 
 cpa_status check_pointers(const cpa_attn_args* a, bool attention) {
-    if (a->total_q > 0 && (!a->k_new || !a->v_new || !a->slot_mapping)) return CPA_ERR_INVALID_ARG;
+    if (a->total_q > 0 && (!a->k_new || !a->v_new)) return CPA_ERR_INVALID_ARG;
+    // without a slot mapping, slots come from the block table
+    if (a->total_q > 0 && !a->slot_mapping &&
+        (!a->cu_seqlens_q || !a->cached_seq_len || !a->block_table || a->num_seqs <= 0 ||
+         a->max_blocks_per_seq <= 0))
+        return CPA_ERR_INVALID_ARG;
     if (!a->k_cache || !a->v_cache) return CPA_ERR_INVALID_ARG;
     if (attention) {
         if (a->total_q > 0 && (!a->q || !a->out)) return CPA_ERR_INVALID_ARG;
@@ -1047,6 +1078,11 @@ cpa_status launch_prep(const cpa_attn_args* a, const Resolved* r, bool plan, hip
     p.k_cache = a->k_cache;
     p.v_cache = a->v_cache;
     p.slots = a->slot_mapping;
+    p.block_table = a->block_table;
+    p.max_blocks = a->max_blocks_per_seq;
+    p.cu = a->cu_seqlens_q;
+    p.cached = a->cached_seq_len;
+    p.num_seqs = a->num_seqs;
     p.total_q = a->total_q;
     p.num_kv_heads = a->num_kv_heads;
     p.block_size = a->block_size;

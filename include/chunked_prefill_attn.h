@@ -107,7 +107,11 @@ typedef struct cpa_attn_args {
     const int32_t* cu_seqlens_q;    /* device                                   */
     const int32_t* cached_seq_len;  /* device                                   */
     const int32_t* block_table;     /* device                                   */
-    const int64_t* slot_mapping;    /* device                                   */
+    const int64_t* slot_mapping;    /* device, or NULL: each active token's slot
+                                       is then block_table[b][p / block_size] *
+                                       block_size + p % block_size, p =
+                                       cached_seq_len[b] + its offset in the
+                                       chunk, the same formula                 */
     void* out;                      /* device                                   */
     float* lse;                     /* device, may be NULL                      */
     void* workspace;                /* device scratch, >= cpa_workspace_bytes() */
@@ -145,7 +149,9 @@ cpa_status cpa_workspace_bytes(const cpa_attn_args* args, size_t* bytes);
  * k_cache/v_cache, bit for bit ("Prefill Processing", section "How
  * Segmentation Works with KV Segments": each iteration writes the KV of its
  * active tokens).  Reads dtype, num_kv_heads, head_dim, block_size,
- * num_blocks, total_q and the five pointers it needs. */
+ * num_blocks, total_q and the five pointers it needs; with slot_mapping NULL
+ * also num_seqs, max_blocks_per_seq, cu_seqlens_q, cached_seq_len and
+ * block_table, from which the slots are derived. */
 cpa_status cpa_reshape_and_cache(const cpa_attn_args* args, void* stream);
 
 /* Cache write plus the device work plan (written into the workspace). */

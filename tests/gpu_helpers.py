@@ -83,9 +83,11 @@ def _dev(a, dt):
 
 
 def gpu_call(cache, batch, q, k_new, v_new, kv_segment_size, *, scale=None, want_lse=False,
-             split_pre=0, split_dec=0, dec_thresh=0, only_cache=False):
+             split_pre=0, split_dec=0, dec_thresh=0, only_cache=False, derive_slots=False):
     """Run one batch through the library.  q/k_new/v_new are CPU or device
-    tensors of the cache dtype.  Returns (out, lse) as CPU tensors."""
+    tensors of the cache dtype.  derive_slots passes no slot mapping (the
+    library derives the slots from the block table).  Returns (out, lse) as
+    CPU tensors."""
     qd = q.to(DEV) if q is not None else None
     kd, vd = k_new.to(DEV), v_new.to(DEV)
     out = torch.empty_like(qd) if qd is not None else None
@@ -96,7 +98,7 @@ def gpu_call(cache, batch, q, k_new, v_new, kv_segment_size, *, scale=None, want
                     cu_seqlens_q=_dev(batch["cu_seqlens_q"], np.int32),
                     cached_seq_len=_dev(batch["cached_seq_len"], np.int32),
                     block_table=_dev(batch["block_table"], np.int32),
-                    slot_mapping=_dev(batch["slot_mapping"], np.int64),
+                    slot_mapping=None if derive_slots else _dev(batch["slot_mapping"], np.int64),
                     h_cu_seqlens_q=batch["cu_seqlens_q"], h_cached_seq_len=batch["cached_seq_len"],
                     kv_segment_size=kv_segment_size, scale=scale, lse=lse,
                     decode_token_threshold=dec_thresh, split_keys_prefill=split_pre,

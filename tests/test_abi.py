@@ -48,6 +48,10 @@ def _args(**over):
     cu = np.array([0, 100, 300], dtype=np.int32)
     cached = np.array([1000, 0], dtype=np.int32)
     keep = [cu, cached]
+    fake = 0x1000   # never dereferenced: only host checks run here
+    for f in ("q", "k_new", "v_new", "k_cache", "v_cache", "cu_seqlens_q", "cached_seq_len",
+              "block_table", "slot_mapping", "out"):
+        setattr(a, f, fake)
     for k, v in over.items():
         if k == "cu":
             cu = np.asarray(v, dtype=np.int32); keep.append(cu)
@@ -56,10 +60,6 @@ def _args(**over):
         else:
             setattr(a, k, v)
     a.h_cu_seqlens_q, a.h_cached_seq_len = cu.ctypes.data, cached.ctypes.data
-    fake = 0x1000   # never dereferenced: only host checks run here
-    for f in ("q", "k_new", "v_new", "k_cache", "v_cache", "cu_seqlens_q", "cached_seq_len",
-              "block_table", "slot_mapping", "out"):
-        setattr(a, f, fake)
     return a, keep
 
 
@@ -122,3 +122,13 @@ def test_missing_workspace_is_refused_before_launch():
 def test_fp32_head_dim_128_is_unsupported():
     a, _keep = _args(dtype=1)
     assert _lib.lib().cpa_check_args(ctypes.byref(a)) == _lib.CPA_ERR_UNSUPPORTED
+
+
+def test_missing_slot_mapping_needs_a_block_table():
+    # without slot_mapping the cache write derives slots from the block table,
+    # so that table (and the sequence descriptors) must be there
+    a, _keep = _args(slot_mapping=0, block_table=0)
+    st = _lib.lib().cpa_reshape_and_cache(ctypes.byref(a), None)
+    assert st == _lib.CPA_ERR_INVALID_ARG
+    a, _keep = _args(slot_mapping=0)
+    assert _lib.lib().cpa_check_args(ctypes.byref(a)) == 0

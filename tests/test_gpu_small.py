@@ -32,7 +32,7 @@ def _resolve(v, S):
     return {"S": S, "2S": 2 * S}.get(v, v)
 
 
-def run_case(case, split, fill=0.0, seed=0):
+def run_case(case, split, fill=0.0, seed=0, derive_slots=False):
     name, dtype, H, G, D, bs, S, reqs, decodes, budget = case
     rng = np.random.default_rng(1000 + seed)
     max_blocks = max(-(-(p + 1) // bs) for p, _ in reqs + [(c + 1, 0) for c in decodes]) + 1
@@ -63,7 +63,8 @@ def run_case(case, split, fill=0.0, seed=0):
     vt, v64 = quantize(rng.standard_normal((T, G, D)), dtype)
     sp, sd = (_resolve(x, S) for x in SPLITS[split])
     say(f"case {name} split={split} T={T} seqs={pb['num_seqs']}")
-    out, _ = gpu_call(pair.cache, pb, qt, kt, vt, S, split_pre=sp, split_dec=sd)
+    out, _ = gpu_call(pair.cache, pb, qt, kt, vt, S, split_pre=sp, split_dec=sd,
+                      derive_slots=derive_slots)
     ref = pair.oracle_batch(ob, q64, k64, v64, 1 / math.sqrt(D), G)
     return pair, out, ref, dtype
 
@@ -75,6 +76,19 @@ def test_small_batches_match_oracle(case, split):
     pair, out, ref, dtype = run_case(case, split)
     assert_close(out.to(torch.float64).numpy(), ref, dtype, f"{case[0]}/{split}")
     # every cache byte: written slots hold the new rows, all others untouched
+    gk, gv = pair.cache.canonical_bits()
+    assert np.array_equal(gk, bits_of(pair.k_pool, dtype))
+    assert np.array_equal(gv, bits_of(pair.v_pool, dtype))
+
+
+@pytest.mark.parametrize("case", [CASES[1], CASES[6], CASES[7], CASES[8]],
+                         ids=["ragged", "fp32", "decodes", "tiny"])
+def test_slots_derived_from_the_block_table(case):
+    # no slot mapping passed: the cache write derives each token's slot from
+    # cu_seqlens_q, cached_seq_len and the block table; same bytes, same outputs
+    need_gpu()
+    pair, out, ref, dtype = run_case(case, "auto", derive_slots=True)
+    assert_close(out.to(torch.float64).numpy(), ref, dtype, f"{case[0]}/derived slots")
     gk, gv = pair.cache.canonical_bits()
     assert np.array_equal(gk, bits_of(pair.k_pool, dtype))
     assert np.array_equal(gv, bits_of(pair.v_pool, dtype))

@@ -530,51 +530,56 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             }
             if (masked) apply_mask(S0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            // P2: max of S0 under the first four S1 MFMAs
+            // Speculative exps: the exps of a 32-key block use the current
+            // reference while its maximum is still being taken; when the
+            // maximum turns out to exceed the reference by more than 8 (rare;
+            // always on an item's first tile), the block's exps are redone
+            // after the rescale.
+            auto ref_nm = [&]() { return (m_run == -INFINITY) ? 0.f : -m_run * sl2e; };
+            auto over = [&](float hm) { return __builtin_amdgcn_ballot_w64((hm - m_run) * sl2e > 8.f) != 0; };
+            float nm = ref_nm();
+            // P2: S1 MFMAs; max and exp of S0
             float hm = -INFINITY;
 #pragma unroll
-            for (int f = 8; f < 12; ++f) {
+            for (int f = 8; f < 16; ++f) {
                 fr[(f + 3) & 3] = frag(f + 3);
                 S1 = E::mma(fr[f & 3], qf[f & 7], S1);
-                const int r = 4 * (f - 8);
+                const int r = 2 * (f - 8);
                 hm = fmaxf(hm, fmaxf(S0[r], S0[r + 1]));
-                hm = fmaxf(hm, fmaxf(S0[r + 2], S0[r + 3]));
+                ex2(S0, r >> 3, r, nm);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            decide(hm);
-            float nm = (m_run == -INFINITY) ? 0.f : -m_run * sl2e;
-            __builtin_amdgcn_sched_barrier(0);
-            // P2: exp of S0 under the last four S1 MFMAs
+            if (over(hm)) {
+                decide(hm);
+                nm = ref_nm();
+                rs = 0.f;
 #pragma unroll
-            for (int f = 12; f < 16; ++f) {
-                fr[(f + 3) & 3] = frag(f + 3);
-                S1 = E::mma(fr[f & 3], qf[f & 7], S1);
-                const int r = 4 * (f - 12);
-                ex2(S0, r >> 3, r, nm);
-                ex2(S0, r >> 3, r + 2, nm);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int r = 0; r < 16; r += 2) ex2(S0, r >> 3, r, nm);
             }
             l_run += rs;                 // before S1's decision may rescale l
             rs = 0.f;
             if (masked) apply_mask(S1, 1);
             __builtin_amdgcn_sched_barrier(0);
-            // P3: PV of the first half with the max of S1
+            // P3: PV of the first half; max of S1 and exp of its registers 0..7
             hm = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 fr[(i + 3) & 3] = frag(16 + i + 3);
                 oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
                 hm = fmaxf(hm, fmaxf(S1[2 * i], S1[2 * i + 1]));
+                if (i < 4) ex2(S1, 2, 2 * i, nm);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            decide(hm);
-            nm = (m_run == -INFINITY) ? 0.f : -m_run * sl2e;
-            __builtin_amdgcn_sched_barrier(0);
-            // P4: exp of S1 registers 0..7, then PV of keys 32..47 under the
-            // exp of registers 8..15, then PV of keys 48..63
+            if (over(hm)) {
+                decide(hm);
+                nm = ref_nm();
+                rs = 0.f;
 #pragma unroll
-            for (int r = 0; r < 8; r += 2) ex2(S1, 2, r, nm);
+                for (int r = 0; r < 8; r += 2) ex2(S1, 2, r, nm);
+            }
             __builtin_amdgcn_sched_barrier(0);
+            // P4: PV of keys 32..47 under the exp of registers 8..15, then PV
+            // of keys 48..63
 #pragma unroll
             for (int i = 8; i < 16; ++i) {
                 if (i + 3 < 16) fr[(i + 3) & 3] = frag(16 + i + 3);

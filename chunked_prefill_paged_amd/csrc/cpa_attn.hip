@@ -59,6 +59,35 @@ constexpr int kKeys = 64;   // keys per LDS tile
 constexpr int kXcds = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// ---------------------------------------------------------------------------
+// Global -> LDS gathers (global_load_lds_dwordx4: each lane's 16 bytes land
+// at M0 + 16 * lane).  They are issued from inline asm so that their
+// completion is awaited only where the kernel says so (s_waitcnt vmcnt
+// before the barrier that publishes a tile): the compiler cannot tell the
+// buffer being filled from the one being read and would otherwise wait for
+// the gather before every LDS read that follows it.
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// wave-uniform 64-bit base, per-lane 32-bit byte offset
+__device__ inline void gather16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+// per-lane 64-bit address
+__device__ inline void gather16(const void* addr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(addr), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima) through the
+// builtin, so that the compiler's own wait insertion knows every vector
+// memory load has completed here and adds none for its loads further on.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <typename T> struct Elem;
 template <> struct Elem<__bf16> {
     static constexpr int kPerChunk = 8;  // elements per 16-byte chunk
@@ -278,47 +307,46 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     // kKeys / 8) table entries the tile spans.  They are loaded one tile
     // ahead, so issuing the gathers never waits on a table read.
     const int nbt = bs >= kKeys ? 1 : (kKeys >> lbs);
+    // (Entries are clamped to the cache where they are used: a clamp here
+    // would wait for the load, and with it for every gather issued before.)
     auto load_bt = [&](int ts) -> int {
-        return (int)min((uint32_t)bt[(ts >> lbs) + min(lane, nbt - 1)], nb_max);
+        return bt[(ts >> lbs) + min(lane, nbt - 1)];
     };
     const char* kc_g = (const char*)(kc + (size_t)g * bs * D);
     const char* vc_g = (const char*)(vc + (size_t)g * D * bs);
     const uint32_t blk_bytes = (uint32_t)(G * bs * D * (int)sizeof(T));
     auto dma_k = [&](int ts, int buf, int btv) {
+        const uint32_t lds0 = lds_addr(&lds_k[buf][0]);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int sl = wave * NLD + i;
             const int kt = sl * RK;                        // first key of the slab within the tile
-            const uint32_t blk = (uint32_t)__builtin_amdgcn_readlane(btv, bs >= kKeys ? 0 : (kt >> lbs));
-            const char* base = kc_g + (size_t)blk * blk_bytes;
-            const uint32_t off = (uint32_t)(((ts + kt) & (bs - 1)) * (D * (int)sizeof(T)))
-                               + (uint32_t)(k_dma_off[i] * (int)sizeof(T));
-            __builtin_amdgcn_global_load_lds((const void*)(base + off),
-                                             (void*)((char*)&lds_k[buf][0] + sl * 1024), 16, 0, 0);
+            const uint32_t blk = min((uint32_t)__builtin_amdgcn_readlane(btv, bs >= kKeys ? 0 : (kt >> lbs)), nb_max);
+            const char* base = kc_g + (size_t)blk * blk_bytes + ((ts + kt) & (bs - 1)) * (D * (int)sizeof(T));
+            gather16(base, (uint32_t)(k_dma_off[i] * (int)sizeof(T)), lds0 + sl * 1024);
         }
     };
     auto dma_v = [&](int ts, int buf, int btv) {
+        const uint32_t lds0 = lds_addr(&lds_v[buf][0]);
         if (bs >= kKeys) {
             // the 64 keys of the tile share one block: scalar base, 32-bit lane offsets
-            const uint32_t blk = (uint32_t)__builtin_amdgcn_readlane(btv, 0);
+            const uint32_t blk = min((uint32_t)__builtin_amdgcn_readlane(btv, 0), nb_max);
             const char* base = vc_g + (size_t)blk * blk_bytes + (ts & (bs - 1)) * (int)sizeof(T);
 #pragma unroll
             for (int i = 0; i < NLD; ++i) {
                 const int sl = wave * NLD + i;
                 const uint32_t off = (uint32_t)(((v_d0 + i * RV) * bs + v_dma_key(i)) * (int)sizeof(T));
-                __builtin_amdgcn_global_load_lds((const void*)(base + off),
-                                                 (void*)((char*)&lds_v[buf][0] + sl * 1024), 16, 0, 0);
+                gather16(base, off, lds0 + sl * 1024);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < NLD; ++i) {
                 const int sl = wave * NLD + i;
                 const int kk = v_dma_key(i);                // key offset within the tile (per lane)
-                const uint32_t blk = (uint32_t)__shfl(btv, kk >> lbs);
+                const uint32_t blk = min((uint32_t)__shfl(btv, kk >> lbs), nb_max);
                 const char* base = vc_g + (size_t)blk * blk_bytes;
                 const uint32_t off = (uint32_t)(((v_d0 + i * RV) * bs + ((ts + kk) & (bs - 1))) * (int)sizeof(T));
-                __builtin_amdgcn_global_load_lds((const void*)(base + off),
-                                                 (void*)((char*)&lds_v[buf][0] + sl * 1024), 16, 0, 0);
+                gather16(base + off, lds0 + sl * 1024);
             }
         }
     };
@@ -609,6 +637,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             dma_v(tstart(0), 0, bt0);
         }
         if (nfull > 1) btn = load_bt(tstart(1));
+        wait_vmem();                     // Q and the first block ids
         for (int u = 0; u < ntiles; ++u) {
             const int ts = tstart(u);
             const int buf = u & 1;
@@ -618,7 +647,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             }
             // this tile's gathers have landed (each wave waits for its own,
             // the barrier for everyone's); all waves are done with buf ^ 1
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            wait_vmem();
             __syncthreads();
             if (u + 1 < nfull) {
                 dma_k(tstart(u + 1), buf ^ 1, btn);

@@ -20,6 +20,11 @@ Everything is written as the plain definition, in float64, from these pages:
 * "vLLM Chunked Prefill 如何改变 KV Cache 管理": incremental block
   allocation (section 2.1), block-aligned budget (section 2.3).
 
+``rope`` adds rotary position embedding at absolute positions ("Prefill
+Optimisation ...", section 2, "Causal equivalence"; "Chunked Prefill",
+section "From scratch"), in the standard rotary form, which the pages name
+but do not write out.
+
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
 against printed values, closed forms, a library routine or an invariant.
 The one reading without a pin of its own is the GQA head grouping (the pages
@@ -27,4 +32,4 @@ never define it); it is fixed to the consecutive grouping that
 ``torch.nn.functional.scaled_dot_product_attention`` uses and is pinned only
 against that library convention.
 """
-from . import attention, counters, schedule  # noqa: F401
+from . import attention, counters, rope, schedule  # noqa: F401

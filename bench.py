@@ -52,9 +52,10 @@ def _args():
     ap.add_argument("--split-keys-prefill", type=int, default=0,
                     help="0 automatic, -1 never, else keys per work item")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("c2", "c4", "c5"), default="c2",
+    ap.add_argument("--workload", choices=("c2", "c4", "c5", "rope"), default="c2",
                     help="c2: the 10k prompt (headline line); c5: the 32k prompt, per chunk "
-                         "and against one monolithic call; c4: the mixed decode + prefill batch")
+                         "and against one monolithic call; c4: the mixed decode + prefill batch; "
+                         "rope: the cache write with rotary embedding fused in, at two chunk shapes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device-to-device copy 5 times and exit")
     return ap.parse_args()
@@ -411,6 +412,76 @@ def run_mixed_batch(args):
     }), flush=True)
 
 
+def run_rope(args):
+    """The cache write alone and with rotary embedding fused in (queries
+    rotated into a second tensor, keys rotated on their way into the cache),
+    at two chunk shapes: a 2048-token chunk of the 10k prompt (H32/G8, bs128,
+    cached 2048) and the last 2048-token chunk of the 32k prompt (H64/G8,
+    bs16, cached 30,720).  HBM-bound: reports GB/s of the bytes each call
+    must move (K/V read and written; with RoPE also Q read and written)."""
+    import torch
+    from chunked_prefill_paged_amd import AttnCall, cache_shapes
+    from chunked_prefill_paged_amd.attention import Rope
+
+    dev = "cuda"
+    shapes = [("10k prompt chunk: T2048 at cached 2048, H32/G8/D128, bs128", 2048, 2048, 32, 8, 128, 128),
+              ("32k prompt last chunk: T2048 at cached 30720, H64/G8/D128, bs16", 2048, 30720, 64, 8, 128, 16)]
+    steps, warm = max(1, args.steps), max(1, args.warmup)
+    res = []
+    for name, T, c, H, G, D, bs in shapes:
+        nb = (c + T) // bs
+        ks, vs = cache_shapes(nb, G, bs, D)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(11)
+        k_cache = torch.zeros(ks, dtype=torch.bfloat16, device=dev)
+        v_cache = torch.zeros(vs, dtype=torch.bfloat16, device=dev)
+        q = torch.randn((T, H, D), generator=gen, device=dev).to(torch.bfloat16)
+        kn = torch.randn((T, G, D), generator=gen, device=dev).to(torch.bfloat16)
+        vn = torch.randn((T, G, D), generator=gen, device=dev).to(torch.bfloat16)
+        q_out = torch.empty_like(q)
+        table = torch.from_numpy(np.random.default_rng(12).permutation(nb).astype(np.int32)[None, :]).to(dev)
+        call = AttnCall(q=q, k_new=kn, v_new=vn, k_cache=k_cache, v_cache=v_cache, out=q_out,
+                        cu_seqlens_q=torch.tensor([0, T], dtype=torch.int32, device=dev),
+                        cached_seq_len=torch.tensor([c], dtype=torch.int32, device=dev),
+                        block_table=table, slot_mapping=None,
+                        h_cu_seqlens_q=np.array([0, T], np.int32), h_cached_seq_len=np.array([c], np.int32),
+                        kv_segment_size=1024 if bs == 128 else 4096)
+        rope = Rope(q_out, 10000.0)
+        kv_bytes = 2 * 2 * T * G * D * 2              # K and V, read once and written once
+        q_bytes = 2 * T * H * D * 2                   # Q read, rotated Q written
+        row = {"shape": name}
+        for label, fn, nbytes in (("cache_write", lambda: call.reshape_and_cache(), kv_bytes),
+                                  ("rope_cache_write", lambda: call.rope_reshape_and_cache(rope),
+                                   kv_bytes + q_bytes)):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for _ in range(warm):
+                fn()
+            torch.cuda.synchronize()
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            us = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
+            row[label] = {"us": round(us, 2), "mb": round(nbytes / 1e6, 2),
+                          "gbps": round(nbytes / us / 1e3, 1),
+                          "frac_of_hbm_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+        res.append(row)
+    r0 = res[0]["rope_cache_write"]
+    print(json.dumps({
+        "metric": "cache write with rotary embedding fused: GB/s of the bytes it must move",
+        "value": r0["gbps"], "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(r0["us"] / 1e3, 5), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": res[0]["shape"] + "; RoPE theta 10000, rotate-half pairs"},
+        "roofline": {"bound": "hbm", "achieved": r0["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": r0["frac_of_hbm_peak"], "traffic": None,
+                     "kernel": "prep_kernel<bf16,128,rope>"},
+        "shapes": res,
+    }), flush=True)
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -429,6 +500,9 @@ def main():
         return
     if args.workload == "c4":
         run_mixed_batch(args)
+        return
+    if args.workload == "rope":
+        run_rope(args)
         return
     bench = PromptBench(args.kv_segment_size, args.split_keys_prefill)
     flops = bench.flops_per_step()

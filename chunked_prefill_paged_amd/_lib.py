@@ -45,6 +45,10 @@ class AttnArgs(ctypes.Structure):
     ]
 
 
+class RopeArgs(ctypes.Structure):
+    _fields_ = [("theta", ctypes.c_float), ("interleaved", _i32), ("q_out", _vp)]
+
+
 class PlanInfo(ctypes.Structure):
     _fields_ = [("num_items", _i32), ("num_merge_rows", _i32), ("num_partials", _i64),
                 ("split_keys_prefill", _i32), ("split_keys_decode", _i32),
@@ -75,6 +79,9 @@ SIGNATURES = {
     "cpa_prepare": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _vp]),
     "cpa_attention": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _vp]),
     "cpa_chunked_prefill_attn": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _vp]),
+    "cpa_rope_reshape_and_cache": (ctypes.c_int, [ctypes.POINTER(AttnArgs), ctypes.POINTER(RopeArgs), _vp]),
+    "cpa_rope_prepare": (ctypes.c_int, [ctypes.POINTER(AttnArgs), ctypes.POINTER(RopeArgs), _vp]),
+    "cpa_rope_chunked_prefill_attn": (ctypes.c_int, [ctypes.POINTER(AttnArgs), ctypes.POINTER(RopeArgs), _vp]),
     "cpa_schedule_prompt": (ctypes.c_int, [_i32, _i32, _i64, _i32, _i32, _p_i32, _i32, _p_i32]),
     "cpa_sched_create": (ctypes.c_int, [ctypes.POINTER(SchedConfig), ctypes.POINTER(_vp)]),
     "cpa_sched_destroy": (None, [_vp]),

@@ -126,3 +126,33 @@ class AttnCall:
     def __call__(self, stream=None) -> None:
         _lib.check(_lib.lib().cpa_chunked_prefill_attn(ctypes.byref(self.args), _stream(stream)),
                    "cpa_chunked_prefill_attn")
+
+    # rotary position embedding fused into the cache write (``rope`` is a
+    # ``Rope``); the rotated queries land in ``rope.q_out``
+    def rope_reshape_and_cache(self, rope, stream=None) -> None:
+        _lib.check(_lib.lib().cpa_rope_reshape_and_cache(ctypes.byref(self.args),
+                                                         ctypes.byref(rope.args), _stream(stream)),
+                   "cpa_rope_reshape_and_cache")
+
+    def rope_prepare(self, rope, stream=None) -> None:
+        _lib.check(_lib.lib().cpa_rope_prepare(ctypes.byref(self.args), ctypes.byref(rope.args),
+                                               _stream(stream)), "cpa_rope_prepare")
+
+    def rope_call(self, rope, stream=None) -> None:
+        _lib.check(_lib.lib().cpa_rope_chunked_prefill_attn(ctypes.byref(self.args),
+                                                            ctypes.byref(rope.args),
+                                                            _stream(stream)),
+                   "cpa_rope_chunked_prefill_attn")
+
+
+class Rope:
+    """Rotary-embedding parameters: base ``theta``, pairing (``interleaved``
+    False: element i with i + D/2; True: 2i with 2i + 1) and the tensor that
+    receives the rotated queries (may be the query tensor itself)."""
+
+    def __init__(self, q_out, theta: float = 10000.0, interleaved: bool = False):
+        self._keep = q_out
+        self.args = _lib.RopeArgs()
+        self.args.theta = float(theta)
+        self.args.interleaved = 1 if interleaved else 0
+        self.args.q_out = _ptr(q_out)

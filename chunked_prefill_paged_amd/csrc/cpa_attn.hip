@@ -791,6 +791,13 @@ struct PrepParams {
     int32_t log2_bs;
     int32_t num_blocks;
     int32_t cache_wgs;
+    // rotary embedding (rope != 0): 1 pairs element i with i + D/2, 2 pairs
+    // 2i with 2i + 1; q rows of the workgroup's KV-head group are rotated
+    // into q_out, keys on their way into the cache
+    int32_t rope;
+    float rope_theta;
+    const void* q;
+    void* q_out;
     // plan (only when plan != 0)
     int32_t plan;
     const int32_t* cu;
@@ -814,8 +821,59 @@ static_assert(kMaxSeqs <= 65536, "sequence ids are held as 16-bit values in the 
 // Rows of 64 new tokens of KV head g go to their slots.  K rows are copied
 // with 16-byte stores; V is staged in LDS and written as columns of the
 // transposed layout, lanes over tokens so that neighbouring slots coalesce.
+//
+// With ROPE, the keys are rotated before they are stored and the query rows
+// of the group's heads are rotated into q_out, every token at its absolute
+// position cached_seq_len[b] + (offset in its chunk) ("Prefill Optimisation
+// ...", section 2, "Causal equivalence": positional encodings use absolute
+// positions; "Chunked Prefill", "From scratch": the cached length is the
+// position offset).  The pages name rotary embedding without writing it
+// out; this is the standard form: pair i of a head turns by p * theta^(-2i/D)
+// radians, (x, y) -> (x cos - y sin, x sin + y cos).  The workgroup's
+// cos/sin table (64 tokens x D/2 pairs) is built once in LDS; angles are
+// taken in double precision, since p * theta^(-2i/D) reaches tens of
+// thousands of radians, then rounded to float.
 template <typename T, int D>
-__device__ void cache_write(const PrepParams& p, char* smem) {
+__device__ inline void rope_rows(const T* src, T* dst, int ch, const float2* cs, bool interleaved) {
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr int NCK = D / EPC;
+    // unit ch covers pairs ch*EPC .. ch*EPC + EPC - 1 of the row: chunks ch
+    // and ch + NCK/2 (rotate-half) or chunks 2ch and 2ch + 1 (interleaved)
+    const int ca = interleaved ? 2 * ch : ch;
+    const int cb = interleaved ? 2 * ch + 1 : ch + NCK / 2;
+    u32x4 ua = *(const u32x4*)(src + ca * EPC);
+    u32x4 ub = *(const u32x4*)(src + cb * EPC);
+    T va[EPC], vb[EPC];
+    __builtin_memcpy(va, &ua, 16);
+    __builtin_memcpy(vb, &ub, 16);
+    float x[2 * EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+        x[e] = (float)va[e];
+        x[EPC + e] = (float)vb[e];
+    }
+    float y[2 * EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+        const int i0 = interleaved ? 2 * e : e;
+        const int i1 = interleaved ? 2 * e + 1 : EPC + e;
+        const float2 c = cs[ch * EPC + e];
+        y[i0] = __builtin_fmaf(x[i0], c.x, -x[i1] * c.y);
+        y[i1] = __builtin_fmaf(x[i0], c.y, x[i1] * c.x);
+    }
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+        va[e] = (T)y[e];
+        vb[e] = (T)y[EPC + e];
+    }
+    __builtin_memcpy(&ua, va, 16);
+    __builtin_memcpy(&ub, vb, 16);
+    *(u32x4*)(dst + ca * EPC) = ua;
+    *(u32x4*)(dst + cb * EPC) = ub;
+}
+
+template <typename T, int D, bool ROPE>
+__device__ void cache_write(const PrepParams& p, char* smem, float2* s_cs) {
     constexpr int EPC = 16 / sizeof(T);
     constexpr int NCK = D / EPC;
     constexpr int LD = D + 4 / (int)sizeof(T);   // LDS pitch: one extra 32-bit word
@@ -835,41 +893,84 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
     // token's sequence b by binary search over cu_seqlens_q, position
     // cached_seq_len[b] + offset in its chunk)
     __shared__ int64_t s_slot[64];
+    __shared__ int s_pos[64];
     if (tid < ntok) {
         const int tok = tok0 + tid;
-        int64_t slot;
-        if (p.slots) {
-            slot = p.slots[tok];
-        } else {
-            int lo = 0, hi = p.num_seqs;          // cu[lo] <= tok < cu[hi]
+        int64_t slot = 0;
+        int lo = 0, pos = 0;
+        if (ROPE || !p.slots) {
+            int hi = p.num_seqs;                  // cu[lo] <= tok < cu[hi]
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
                 if (p.cu[mid] <= tok) lo = mid; else hi = mid;
             }
-            const int pos = p.cached[lo] + (tok - p.cu[lo]);
+            pos = p.cached[lo] + (tok - p.cu[lo]);
+        }
+        if (p.slots) {
+            slot = p.slots[tok];
+        } else {
             const int col = pos >> p.log2_bs;
             slot = col < p.max_blocks
                        ? (int64_t)p.block_table[(size_t)lo * p.max_blocks + col] * bs + (pos & (bs - 1))
                        : -1;
         }
         s_slot[tid] = slot;
+        s_pos[tid] = pos;
+    }
+    if constexpr (ROPE) {
+        // theta^(-2i/D) for the D/2 pairs, then cos/sin of every (token, pair)
+        __shared__ double s_freq[D / 2];
+        if (tid < D / 2) s_freq[tid] = pow((double)p.rope_theta, -2.0 * tid / D);
+        __syncthreads();
+        for (int idx = tid; idx < ntok * (D / 2); idx += kThreads) {
+            const int tk = idx / (D / 2), i = idx - tk * (D / 2);
+            double sn, cn;
+            sincos((double)s_pos[tk] * s_freq[i], &sn, &cn);
+            s_cs[idx] = make_float2((float)cn, (float)sn);
+        }
     }
     __syncthreads();
+    const bool inter = ROPE && p.rope == 2;
+    if constexpr (ROPE) {
+        // keys: rotate, then store at the slot
+        for (int u = tid; u < ntok * (NCK / 2); u += kThreads) {
+            const int tk = u / (NCK / 2), ch = u - tk * (NCK / 2);
+            const int64_t slot = s_slot[tk];
+            if (slot >= 0 && slot < nslots) {
+                const int64_t blk = slot >> p.log2_bs;
+                const int off = (int)(slot & (bs - 1));
+                rope_rows<T, D>(kn + ((size_t)(tok0 + tk) * G + g) * D,
+                                kc + ((blk * G + g) * bs + off) * D, ch, s_cs + tk * (D / 2), inter);
+            }
+        }
+        // queries of the group's heads
+        const int hpg = p.num_heads / G;
+        const T* qs = (const T*)p.q;
+        T* qd = (T*)p.q_out;
+        for (int u = tid; u < ntok * hpg * (NCK / 2); u += kThreads) {
+            const int row = u / (NCK / 2), ch = u - row * (NCK / 2);
+            const int tk = row / hpg, h = g * hpg + (row - tk * hpg);
+            const size_t r = ((size_t)(tok0 + tk) * p.num_heads + h) * D;
+            rope_rows<T, D>(qs + r, qd + r, ch, s_cs + tk * (D / 2), inter);
+        }
+    }
     for (int cidx = tid; cidx < ntok * NCK; cidx += kThreads) {
         const int tk = cidx / NCK, ch = cidx - (cidx / NCK) * NCK;
         const size_t src = ((size_t)(tok0 + tk) * G + g) * D + ch * EPC;
-        const u32x4 kv = *(const u32x4*)(kn + src);
         const u32x4 vv = *(const u32x4*)(vn + src);
         uint32_t* dst = (uint32_t*)(tile + tk * LD + ch * EPC);
         dst[0] = vv.x;
         dst[1] = vv.y;
         dst[2] = vv.z;
         dst[3] = vv.w;
-        const int64_t slot = s_slot[tk];
-        if (slot >= 0 && slot < nslots) {
-            const int64_t blk = slot >> p.log2_bs;
-            const int off = (int)(slot & (bs - 1));
-            *(u32x4*)(kc + ((blk * G + g) * bs + off) * D + ch * EPC) = kv;
+        if constexpr (!ROPE) {
+            const u32x4 kv = *(const u32x4*)(kn + src);
+            const int64_t slot = s_slot[tk];
+            if (slot >= 0 && slot < nslots) {
+                const int64_t blk = slot >> p.log2_bs;
+                const int off = (int)(slot & (bs - 1));
+                *(u32x4*)(kc + ((blk * G + g) * bs + off) * D + ch * EPC) = kv;
+            }
         }
     }
     __syncthreads();
@@ -1000,14 +1101,15 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
     }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(kThreads) void prep_kernel(const PrepParams p) {
     __shared__ __attribute__((aligned(16))) char smem[kPrepSmem];
+    __shared__ float2 s_cs[ROPE ? 64 * (D / 2) : 1];
     if ((int)blockIdx.x >= p.cache_wgs) {
         build_plan(p, smem);
         return;
     }
-    cache_write<T, D>(p, smem);
+    cache_write<T, D, ROPE>(p, smem, s_cs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1105,7 +1207,8 @@ cpa_status check_pointers(const cpa_attn_args* a, bool attention) {
 }
 
 template <typename T, int D>
-cpa_status launch_prep(const cpa_attn_args* a, const Resolved* r, bool plan, hipStream_t stream) {
+cpa_status launch_prep(const cpa_attn_args* a, const Resolved* r, bool plan, const cpa_rope_args* rope,
+                       hipStream_t stream) {
     PrepParams p{};
     p.k_new = a->k_new;
     p.v_new = a->v_new;
@@ -1139,9 +1242,19 @@ cpa_status launch_prep(const cpa_attn_args* a, const Resolved* r, bool plan, hip
         p.items = (int4*)(ws + r->ws.items);
         p.merge = (int2*)(ws + r->ws.merge);
     }
+    p.num_heads = a->num_heads;
+    if (rope) {
+        p.rope = rope->interleaved ? 2 : 1;
+        p.rope_theta = rope->theta;
+        p.q = a->q;
+        p.q_out = rope->q_out;
+    }
     const int grid = p.cache_wgs + (plan ? 1 : 0);
     if (grid == 0) return CPA_OK;
-    hipLaunchKernelGGL((prep_kernel<T, D>), dim3(grid), dim3(kThreads), 0, stream, p);
+    if (rope)
+        hipLaunchKernelGGL((prep_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((prep_kernel<T, D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError() == hipSuccess ? CPA_OK : CPA_ERR_HIP;
 }
 
@@ -1205,15 +1318,26 @@ using namespace cpa;
 
 namespace {
 
-template <typename T, int D>
-cpa_status run_prep(const cpa_attn_args* a, const Resolved* r, bool plan, hipStream_t s) {
-    return launch_prep<T, D>(a, r, plan, s);
+cpa_status prep_dispatch(const cpa_attn_args* a, const Resolved* r, bool plan, const cpa_rope_args* rope,
+                         hipStream_t s) {
+    if (a->dtype == CPA_BF16)
+        return a->head_dim == 128 ? launch_prep<__bf16, 128>(a, r, plan, rope, s)
+                                  : launch_prep<__bf16, 64>(a, r, plan, rope, s);
+    return a->head_dim == 128 ? launch_prep<float, 128>(a, r, plan, rope, s)
+                              : launch_prep<float, 64>(a, r, plan, rope, s);
 }
 
-cpa_status prep_dispatch(const cpa_attn_args* a, const Resolved* r, bool plan, hipStream_t s) {
-    if (a->dtype == CPA_BF16)
-        return a->head_dim == 128 ? run_prep<__bf16, 128>(a, r, plan, s) : run_prep<__bf16, 64>(a, r, plan, s);
-    return a->head_dim == 128 ? run_prep<float, 128>(a, r, plan, s) : run_prep<float, 64>(a, r, plan, s);
+// Host-visible checks of a rotary-embedding request: positions come from
+// cu_seqlens_q and cached_seq_len, so those are needed even with slots.
+cpa_status check_rope(const cpa_attn_args* a, const cpa_rope_args* rope) {
+    if (!rope) return CPA_ERR_INVALID_ARG;
+    if (!std::isfinite(rope->theta) || !(rope->theta > 0.f)) return CPA_ERR_INVALID_ARG;
+    if (rope->interleaved != 0 && rope->interleaved != 1) return CPA_ERR_INVALID_ARG;
+    if (a->num_heads <= 0 || a->num_heads % a->num_kv_heads != 0) return CPA_ERR_INVALID_ARG;
+    if (a->total_q > 0 && (!a->q || !rope->q_out || !a->cu_seqlens_q || !a->cached_seq_len ||
+                           a->num_seqs <= 0))
+        return CPA_ERR_INVALID_ARG;
+    return CPA_OK;
 }
 
 cpa_status attn_dispatch(const cpa_attn_args* a, const Resolved* r, hipStream_t s) {
@@ -1285,7 +1409,7 @@ cpa_status cpa_reshape_and_cache(const cpa_attn_args* a, void* stream) {
     if (st != CPA_OK) return st;
     if ((st = check_pointers(a, false)) != CPA_OK) return st;
     Resolved r{};
-    return prep_dispatch(a, &r, false, (hipStream_t)stream);
+    return prep_dispatch(a, &r, false, nullptr, (hipStream_t)stream);
 }
 
 cpa_status cpa_prepare(const cpa_attn_args* a, void* stream) {
@@ -1295,7 +1419,7 @@ cpa_status cpa_prepare(const cpa_attn_args* a, void* stream) {
     if (a->dtype == CPA_FP32 && a->head_dim == 128) return CPA_ERR_UNSUPPORTED;
     if ((st = check_pointers(a, true)) != CPA_OK) return st;
     if ((st = check_workspace(a, &r)) != CPA_OK) return st;
-    return prep_dispatch(a, &r, true, (hipStream_t)stream);
+    return prep_dispatch(a, &r, true, nullptr, (hipStream_t)stream);
 }
 
 cpa_status cpa_attention(const cpa_attn_args* a, void* stream) {
@@ -1311,6 +1435,34 @@ cpa_status cpa_chunked_prefill_attn(const cpa_attn_args* a, void* stream) {
     cpa_status st = cpa_prepare(a, stream);
     if (st != CPA_OK) return st;
     return cpa_attention(a, stream);
+}
+
+cpa_status cpa_rope_reshape_and_cache(const cpa_attn_args* a, const cpa_rope_args* rope, void* stream) {
+    cpa_status st = check_common(a);
+    if (st != CPA_OK) return st;
+    if ((st = check_pointers(a, false)) != CPA_OK) return st;
+    if ((st = check_rope(a, rope)) != CPA_OK) return st;
+    Resolved r{};
+    return prep_dispatch(a, &r, false, rope, (hipStream_t)stream);
+}
+
+cpa_status cpa_rope_prepare(const cpa_attn_args* a, const cpa_rope_args* rope, void* stream) {
+    Resolved r;
+    cpa_status st = resolve(a, &r);
+    if (st != CPA_OK) return st;
+    if (a->dtype == CPA_FP32 && a->head_dim == 128) return CPA_ERR_UNSUPPORTED;
+    if ((st = check_pointers(a, true)) != CPA_OK) return st;
+    if ((st = check_rope(a, rope)) != CPA_OK) return st;
+    if ((st = check_workspace(a, &r)) != CPA_OK) return st;
+    return prep_dispatch(a, &r, true, rope, (hipStream_t)stream);
+}
+
+cpa_status cpa_rope_chunked_prefill_attn(const cpa_attn_args* a, const cpa_rope_args* rope, void* stream) {
+    cpa_status st = cpa_rope_prepare(a, rope, stream);
+    if (st != CPA_OK) return st;
+    cpa_attn_args rotated = *a;
+    rotated.q = rope->q_out;
+    return cpa_attention(&rotated, stream);
 }
 
 }  // extern "C"

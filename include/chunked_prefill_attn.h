@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define CPA_ABI_VERSION 1
+#define CPA_ABI_VERSION 2
 
 typedef enum cpa_status {
     CPA_OK = 0,
@@ -165,6 +165,48 @@ cpa_status cpa_attention(const cpa_attn_args* args, void* stream);
 
 /* cpa_prepare followed by cpa_attention: the whole chunk step. */
 cpa_status cpa_chunked_prefill_attn(const cpa_attn_args* args, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Rotary position embedding fused into the cache write.
+ *
+ * Every active token is rotated at its absolute position p = cached_seq_len[b]
+ * + (its offset in the chunk) ("Prefill Optimisation: Prefix Caching, Chunked
+ * Prefill, and Disaggregation", section 2, "Causal equivalence": positional
+ * encodings take the token's absolute position in the whole sequence;
+ * "Chunked Prefill" blog note, section "From scratch": the cached length is
+ * the position offset of a step's tokens).  The pages name the rotary
+ * embedding without writing it out; the form here is the standard one: pair
+ * i of a head (i = 0 .. head_dim/2 - 1) turns by p * theta^(-2i/head_dim)
+ * radians, (x, y) -> (x cos - y sin, x sin + y cos), computed in float from
+ * cos/sin evaluated in double and rounded to float; results are rounded to
+ * the element type.  Values are not rotated.
+ * ------------------------------------------------------------------- */
+typedef struct cpa_rope_args {
+    float   theta;        /* rotary base, finite and > 0 (10000 is common)    */
+    int32_t interleaved;  /* 0: element i pairs with i + head_dim/2
+                             ("rotate half"); 1: element 2i with 2i + 1      */
+    void*   q_out;        /* device [total_q, num_heads, head_dim], element
+                             type of q: the rotated queries.  May equal
+                             args->q (rotation in place); otherwise the two
+                             must not overlap.                               */
+} cpa_rope_args;
+
+/* Cache write of rotated keys (values unchanged), and the rotated queries
+ * into rope->q_out.  Reads what cpa_reshape_and_cache reads plus q,
+ * num_heads, num_seqs, cu_seqlens_q and cached_seq_len (positions are
+ * needed even when slot_mapping is given).  CPA_ERR_INVALID_ARG for a NULL
+ * rope, a bad theta or interleaved flag, num_heads not a multiple of
+ * num_kv_heads, or a missing pointer. */
+cpa_status cpa_rope_reshape_and_cache(const cpa_attn_args* args, const cpa_rope_args* rope,
+                                      void* stream);
+
+/* cpa_prepare with the rotation above in its cache write. */
+cpa_status cpa_rope_prepare(const cpa_attn_args* args, const cpa_rope_args* rope, void* stream);
+
+/* cpa_rope_prepare, then cpa_attention on the rotated queries (rope->q_out
+ * in place of args->q): the whole chunk step of a rotary model. */
+cpa_status cpa_rope_chunked_prefill_attn(const cpa_attn_args* args, const cpa_rope_args* rope,
+                                         void* stream);
 
 /* ---------------------------------------------------------------------
  * Host scheduler (no device memory).

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), f"{name} declared but not exported"
     assert set(declared) == set(_lib.SIGNATURES), "binding and header disagree"
-    assert lib.cpa_abi_version() == 1
+    assert lib.cpa_abi_version() == 2
 
 
 def test_status_strings():
@@ -132,3 +132,27 @@ def test_missing_slot_mapping_needs_a_block_table():
     assert st == _lib.CPA_ERR_INVALID_ARG
     a, _keep = _args(slot_mapping=0)
     assert _lib.lib().cpa_check_args(ctypes.byref(a)) == 0
+
+
+def _rope(theta=10000.0, interleaved=0, q_out=0x2000):
+    r = _lib.RopeArgs()
+    r.theta, r.interleaved, r.q_out = theta, interleaved, q_out
+    return r
+
+
+@pytest.mark.parametrize("rope,over", [
+    (None, {}),                                   # no rope parameters
+    (_rope(theta=0.0), {}),
+    (_rope(theta=float("nan")), {}),
+    (_rope(interleaved=2), {}),
+    (_rope(q_out=0), {}),                         # nowhere to put the rotated queries
+    (_rope(), {"q": 0}),
+    (_rope(), {"cached_seq_len": 0}),             # positions need the cached lengths
+    (_rope(), {"num_heads": 12}),                 # not a multiple of 8 KV heads
+])
+def test_bad_rope_requests_are_refused(rope, over):
+    a, _keep = _args(**over)
+    p = ctypes.byref(rope) if rope is not None else None
+    assert _lib.lib().cpa_rope_reshape_and_cache(ctypes.byref(a), p, None) == _lib.CPA_ERR_INVALID_ARG
+    assert _lib.lib().cpa_rope_prepare(ctypes.byref(a), p, None) == _lib.CPA_ERR_INVALID_ARG
+    assert _lib.lib().cpa_rope_chunked_prefill_attn(ctypes.byref(a), p, None) == _lib.CPA_ERR_INVALID_ARG

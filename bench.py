@@ -40,6 +40,7 @@ PEAK_HBM_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("chunked_prefill_paged_amd/csrc/cpa_attn.hip", "chunked_prefill_paged_amd/csrc/cpa_plan.h")
 TRAFFIC_FILE = "profiles/attn_kernel_10k_prompt_hbm_traffic.txt"
+ROPE_TRAFFIC_FILE = "profiles/prep_kernel_rope_cache_write.txt"
 COPY_PROBE_BYTES = 1 << 30
 
 
@@ -69,10 +70,11 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per attention launch from the committed counter summary, or
-    None when the kernel sources changed since it was measured."""
-    path = os.path.join(ROOT, TRAFFIC_FILE)
+def recorded_traffic(rel=TRAFFIC_FILE):
+    """HBM bytes per launch of the kernel a committed counter summary covers
+    (by default the attention kernel's), or None when the kernel sources
+    changed since it was measured."""
+    path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -453,17 +455,18 @@ def run_rope(args):
         for label, fn, nbytes in (("cache_write", lambda: call.reshape_and_cache(), kv_bytes),
                                   ("rope_cache_write", lambda: call.rope_reshape_and_cache(rope),
                                    kv_bytes + q_bytes)):
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(steps)]
+            # back-to-back launches between two events: the mean launch
+            # duration (small kernels; a per-launch pair would add its gap)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             for _ in range(warm):
                 fn()
             torch.cuda.synchronize()
-            for a, b in ev:
-                a.record()
+            a.record()
+            for _ in range(steps):
                 fn()
-                b.record()
+            b.record()
             torch.cuda.synchronize()
-            us = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
+            us = a.elapsed_time(b) / steps * 1e3
             row[label] = {"us": round(us, 2), "mb": round(nbytes / 1e6, 2),
                           "gbps": round(nbytes / us / 1e3, 1),
                           "frac_of_hbm_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
@@ -476,7 +479,7 @@ def run_rope(args):
         "data": "synthetic",
         "config": {"workload": res[0]["shape"] + "; RoPE theta 10000, rotate-half pairs"},
         "roofline": {"bound": "hbm", "achieved": r0["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": r0["frac_of_hbm_peak"], "traffic": None,
+                     "frac": r0["frac_of_hbm_peak"], "traffic": recorded_traffic(ROPE_TRAFFIC_FILE),
                      "kernel": "prep_kernel<bf16,128,rope>"},
         "shapes": res,
     }), flush=True)

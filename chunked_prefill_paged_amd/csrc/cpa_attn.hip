@@ -795,6 +795,7 @@ struct PrepParams {
     // 2i with 2i + 1; q rows of the workgroup's KV-head group are rotated
     // into q_out, keys on their way into the cache
     int32_t rope;
+    int32_t rope_wgs;
     float rope_theta;
     const void* q;
     void* q_out;
@@ -815,26 +816,43 @@ struct PrepParams {
 };
 
 constexpr int kPlanSmem = (3 * kMaxSeqs + 2) * 4 + kMaxSeqs * 2;
-constexpr int kPrepSmem = kPlanSmem > 64 * (128 + 1) * 4 ? kPlanSmem : 64 * (128 + 1) * 4;
+constexpr int kPrepSmem = kPlanSmem > 64 * (128 + 1) * 4 ? kPlanSmem : 64 * (128 + 1) * 4;   // >= V tile
 static_assert(kMaxSeqs <= 65536, "sequence ids are held as 16-bit values in the plan builder");
 
-// Rows of 64 new tokens of KV head g go to their slots.  K rows are copied
-// with 16-byte stores; V is staged in LDS and written as columns of the
-// transposed layout, lanes over tokens so that neighbouring slots coalesce.
+// Rows of kCacheTok new tokens of KV head g go to their slots.  K rows are
+// copied with 16-byte stores; V is staged in LDS and written as columns of
+// the transposed layout, lanes over tokens so that neighbouring slots
+// coalesce.
 //
-// With ROPE, the keys are rotated before they are stored and the query rows
-// of the group's heads are rotated into q_out, every token at its absolute
-// position cached_seq_len[b] + (offset in its chunk) ("Prefill Optimisation
-// ...", section 2, "Causal equivalence": positional encodings use absolute
-// positions; "Chunked Prefill", "From scratch": the cached length is the
-// position offset).  The pages name rotary embedding without writing it
-// out; this is the standard form: pair i of a head turns by p * theta^(-2i/D)
-// radians, (x, y) -> (x cos - y sin, x sin + y cos).  The workgroup's
-// cos/sin table (64 tokens x D/2 pairs) is built once in LDS; angles are
-// taken in double precision, since p * theta^(-2i/D) reaches tens of
-// thousands of radians, then rounded to float.
-template <typename T, int D>
-__device__ inline void rope_rows(const T* src, T* dst, int ch, const float2* cs, bool interleaved) {
+// With ROPE, keys are rotated before they are stored, and separate
+// workgroups rotate the queries (kRopeQTok tokens, all heads, each) into
+// q_out; every token turns at its absolute position cached_seq_len[b] +
+// (offset in its chunk) ("Prefill Optimisation ...", section 2, "Causal
+// equivalence": positional encodings use absolute positions; "Chunked
+// Prefill", "From scratch": the cached length is the position offset).  The
+// pages name rotary embedding without writing it out; this is the standard
+// form: pair i of a head turns by p * theta^(-2i/D) radians, (x, y) ->
+// (x cos - y sin, x sin + y cos).  The angle, up to tens of thousands of
+// radians, is formed and reduced to [-pi, pi] in double precision; cos and
+// sin of the reduced angle are then taken in float (error below 2^-22).  A
+// query workgroup shares one cos/sin table among all heads; a cache-write
+// workgroup (one KV head) evaluates each angle where it uses it.
+constexpr int kCacheTok = 64;   // tokens per cache-write workgroup
+constexpr int kRopeQTok = 8;    // tokens per query-rotation workgroup
+
+// cos/sin of angle pos * freq: reduced to [-pi, pi] in double, then float
+__device__ inline float2 rope_cos_sin(int pos, double freq) {
+    const double a = (double)pos * freq;
+    const double r = a - 6.283185307179586477 * rint(a * 0.159154943091895335769);
+    float sn, cn;
+    sincosf((float)r, &sn, &cn);
+    return make_float2(cn, sn);
+}
+
+// Rotation of one unit of a row: pairs ch*EPC .. ch*EPC + EPC - 1; cs(i)
+// gives cos/sin of pair i.
+template <typename T, int D, typename CS>
+__device__ inline void rope_rows(const T* src, T* dst, int ch, CS cs, bool interleaved) {
     constexpr int EPC = 16 / sizeof(T);
     constexpr int NCK = D / EPC;
     // unit ch covers pairs ch*EPC .. ch*EPC + EPC - 1 of the row: chunks ch
@@ -857,7 +875,7 @@ __device__ inline void rope_rows(const T* src, T* dst, int ch, const float2* cs,
     for (int e = 0; e < EPC; ++e) {
         const int i0 = interleaved ? 2 * e : e;
         const int i1 = interleaved ? 2 * e + 1 : EPC + e;
-        const float2 c = cs[ch * EPC + e];
+        const float2 c = cs(ch * EPC + e);
         y[i0] = __builtin_fmaf(x[i0], c.x, -x[i1] * c.y);
         y[i1] = __builtin_fmaf(x[i0], c.y, x[i1] * c.x);
     }
@@ -872,16 +890,34 @@ __device__ inline void rope_rows(const T* src, T* dst, int ch, const float2* cs,
     *(u32x4*)(dst + cb * EPC) = ub;
 }
 
+// Absolute position of token tok: its sequence b by binary search over
+// cu_seqlens_q, then cached_seq_len[b] + (tok - cu[b]).  *seq receives b.
+__device__ inline int token_position(const PrepParams& p, int tok, int* seq) {
+    int lo = 0, hi = p.num_seqs;                  // cu[lo] <= tok < cu[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.cu[mid] <= tok) lo = mid; else hi = mid;
+    }
+    *seq = lo;
+    return p.cached[lo] + (tok - p.cu[lo]);
+}
+
+// theta^(-2i/D) of the D/2 pairs, in double
+template <int D>
+__device__ void rope_freqs(const PrepParams& p, double* s_freq) {
+    if (threadIdx.x < D / 2) s_freq[threadIdx.x] = pow((double)p.rope_theta, -2.0 * threadIdx.x / D);
+}
+
 template <typename T, int D, bool ROPE>
-__device__ void cache_write(const PrepParams& p, char* smem, float2* s_cs) {
+__device__ void cache_write(const PrepParams& p, char* smem) {
     constexpr int EPC = 16 / sizeof(T);
     constexpr int NCK = D / EPC;
     constexpr int LD = D + 4 / (int)sizeof(T);   // LDS pitch: one extra 32-bit word
     T* tile = (T*)smem;
     const int G = p.num_kv_heads;
     const int grp = blockIdx.x / G, g = blockIdx.x - grp * G;
-    const int tok0 = grp * 64;
-    const int ntok = min(64, p.total_q - tok0);
+    const int tok0 = grp * kCacheTok;
+    const int ntok = min(kCacheTok, p.total_q - tok0);
     const int tid = threadIdx.x;
     const T* kn = (const T*)p.k_new;
     const T* vn = (const T*)p.v_new;
@@ -889,69 +925,44 @@ __device__ void cache_write(const PrepParams& p, char* smem, float2* s_cs) {
     T* vc = (T*)p.v_cache;
     const int bs = p.block_size;
     const int64_t nslots = (int64_t)p.num_blocks * bs;
-    // slots of the 64 tokens: given, or derived from the block table (the
-    // token's sequence b by binary search over cu_seqlens_q, position
-    // cached_seq_len[b] + offset in its chunk)
-    __shared__ int64_t s_slot[64];
-    __shared__ int s_pos[64];
+    // slots of the tokens: given, or derived from the block table at the
+    // token's position
+    __shared__ int64_t s_slot[kCacheTok];
+    __shared__ int s_pos[kCacheTok];
     if (tid < ntok) {
         const int tok = tok0 + tid;
         int64_t slot = 0;
-        int lo = 0, pos = 0;
-        if (ROPE || !p.slots) {
-            int hi = p.num_seqs;                  // cu[lo] <= tok < cu[hi]
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (p.cu[mid] <= tok) lo = mid; else hi = mid;
-            }
-            pos = p.cached[lo] + (tok - p.cu[lo]);
-        }
+        int seq = 0, pos = 0;
+        if (ROPE || !p.slots) pos = token_position(p, tok, &seq);
         if (p.slots) {
             slot = p.slots[tok];
         } else {
             const int col = pos >> p.log2_bs;
             slot = col < p.max_blocks
-                       ? (int64_t)p.block_table[(size_t)lo * p.max_blocks + col] * bs + (pos & (bs - 1))
+                       ? (int64_t)p.block_table[(size_t)seq * p.max_blocks + col] * bs + (pos & (bs - 1))
                        : -1;
         }
         s_slot[tid] = slot;
         s_pos[tid] = pos;
     }
-    if constexpr (ROPE) {
-        // theta^(-2i/D) for the D/2 pairs, then cos/sin of every (token, pair)
-        __shared__ double s_freq[D / 2];
-        if (tid < D / 2) s_freq[tid] = pow((double)p.rope_theta, -2.0 * tid / D);
-        __syncthreads();
-        for (int idx = tid; idx < ntok * (D / 2); idx += kThreads) {
-            const int tk = idx / (D / 2), i = idx - tk * (D / 2);
-            double sn, cn;
-            sincos((double)s_pos[tk] * s_freq[i], &sn, &cn);
-            s_cs[idx] = make_float2((float)cn, (float)sn);
-        }
-    }
+    __shared__ double s_freq[ROPE ? D / 2 : 1];
+    if constexpr (ROPE) rope_freqs<D>(p, s_freq);
     __syncthreads();
-    const bool inter = ROPE && p.rope == 2;
     if constexpr (ROPE) {
-        // keys: rotate, then store at the slot
+        // keys: rotate, then store at the slot (one KV head per workgroup,
+        // so each (token, pair) angle is used once: no table)
+        const bool inter = p.rope == 2;
         for (int u = tid; u < ntok * (NCK / 2); u += kThreads) {
             const int tk = u / (NCK / 2), ch = u - tk * (NCK / 2);
             const int64_t slot = s_slot[tk];
             if (slot >= 0 && slot < nslots) {
                 const int64_t blk = slot >> p.log2_bs;
                 const int off = (int)(slot & (bs - 1));
+                const int pos = s_pos[tk];
                 rope_rows<T, D>(kn + ((size_t)(tok0 + tk) * G + g) * D,
-                                kc + ((blk * G + g) * bs + off) * D, ch, s_cs + tk * (D / 2), inter);
+                                kc + ((blk * G + g) * bs + off) * D, ch,
+                                [&](int i) { return rope_cos_sin(pos, s_freq[i]); }, inter);
             }
-        }
-        // queries of the group's heads
-        const int hpg = p.num_heads / G;
-        const T* qs = (const T*)p.q;
-        T* qd = (T*)p.q_out;
-        for (int u = tid; u < ntok * hpg * (NCK / 2); u += kThreads) {
-            const int row = u / (NCK / 2), ch = u - row * (NCK / 2);
-            const int tk = row / hpg, h = g * hpg + (row - tk * hpg);
-            const size_t r = ((size_t)(tok0 + tk) * p.num_heads + h) * D;
-            rope_rows<T, D>(qs + r, qd + r, ch, s_cs + tk * (D / 2), inter);
         }
     }
     for (int cidx = tid; cidx < ntok * NCK; cidx += kThreads) {
@@ -974,15 +985,55 @@ __device__ void cache_write(const PrepParams& p, char* smem, float2* s_cs) {
         }
     }
     __syncthreads();
+    // V columns: kCacheTok lanes over tokens, the rest of the wave over d
+    constexpr int kLanesD = 64 / kCacheTok;
     const int lane = tid & 63, wave = tid >> 6;
-    if (lane < ntok) {
-        const int64_t slot = s_slot[lane];
+    const int tk = lane % kCacheTok;
+    if (tk < ntok) {
+        const int64_t slot = s_slot[tk];
         if (slot >= 0 && slot < nslots) {
             const int64_t blk = slot >> p.log2_bs;
             const int off = (int)(slot & (bs - 1));
             T* col = vc + (blk * G + g) * D * (int64_t)bs + off;
-            for (int d = wave; d < D; d += 4) col[(size_t)d * bs] = tile[lane * LD + d];
+            for (int d = wave * kLanesD + lane / kCacheTok; d < D; d += 4 * kLanesD)
+                col[(size_t)d * bs] = tile[tk * LD + d];
         }
+    }
+}
+
+// Rotation of the queries of kRopeQTok tokens (all heads) into q_out, from
+// a cos/sin table of the tokens x D/2 pairs shared by the heads.
+template <typename T, int D>
+__device__ void rope_queries(const PrepParams& p, int qgrp) {
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr int NCK = D / EPC;
+    __shared__ int s_pos[kRopeQTok];
+    __shared__ double s_freq[D / 2];
+    __shared__ float2 s_cs[kRopeQTok * (D / 2)];
+    const int tid = threadIdx.x;
+    const int tok0 = qgrp * kRopeQTok;
+    const int ntok = min(kRopeQTok, p.total_q - tok0);
+    if (tid < ntok) {
+        int seq;
+        s_pos[tid] = token_position(p, tok0 + tid, &seq);
+    }
+    rope_freqs<D>(p, s_freq);
+    __syncthreads();
+    for (int idx = tid; idx < ntok * (D / 2); idx += kThreads) {
+        const int tk = idx / (D / 2), i = idx - tk * (D / 2);
+        s_cs[idx] = rope_cos_sin(s_pos[tk], s_freq[i]);
+    }
+    __syncthreads();
+    const bool inter = p.rope == 2;
+    const int H = p.num_heads;
+    const T* qs = (const T*)p.q;
+    T* qd = (T*)p.q_out;
+    for (int u = tid; u < ntok * H * (NCK / 2); u += kThreads) {
+        const int row = u / (NCK / 2), ch = u - row * (NCK / 2);
+        const int tk = row / H;
+        const size_t r = ((size_t)tok0 * H + row) * D;
+        const float2* cs = s_cs + tk * (D / 2);
+        rope_rows<T, D>(qs + r, qd + r, ch, [&](int i) { return cs[i]; }, inter);
     }
 }
 
@@ -1101,15 +1152,23 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
     }
 }
 
+// Grid: cache_wgs cache-write workgroups, then (with ROPE) rope_wgs
+// query-rotation workgroups, then (with a plan) one plan builder.
 template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(kThreads) void prep_kernel(const PrepParams p) {
     __shared__ __attribute__((aligned(16))) char smem[kPrepSmem];
-    __shared__ float2 s_cs[ROPE ? 64 * (D / 2) : 1];
-    if ((int)blockIdx.x >= p.cache_wgs) {
-        build_plan(p, smem);
+    const int wg = blockIdx.x;
+    if (wg < p.cache_wgs) {
+        cache_write<T, D, ROPE>(p, smem);
         return;
     }
-    cache_write<T, D, ROPE>(p, smem, s_cs);
+    if constexpr (ROPE) {
+        if (wg < p.cache_wgs + p.rope_wgs) {
+            rope_queries<T, D>(p, wg - p.cache_wgs);
+            return;
+        }
+    }
+    build_plan(p, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1225,7 +1284,7 @@ cpa_status launch_prep(const cpa_attn_args* a, const Resolved* r, bool plan, con
     p.block_size = a->block_size;
     p.log2_bs = ilog2(a->block_size);
     p.num_blocks = a->num_blocks;
-    p.cache_wgs = ((a->total_q + 63) / 64) * a->num_kv_heads;
+    p.cache_wgs = ((a->total_q + kCacheTok - 1) / kCacheTok) * a->num_kv_heads;
     p.plan = plan ? 1 : 0;
     if (plan) {
         char* ws = (char*)a->workspace;
@@ -1245,11 +1304,12 @@ cpa_status launch_prep(const cpa_attn_args* a, const Resolved* r, bool plan, con
     p.num_heads = a->num_heads;
     if (rope) {
         p.rope = rope->interleaved ? 2 : 1;
+        p.rope_wgs = (a->total_q + kRopeQTok - 1) / kRopeQTok;
         p.rope_theta = rope->theta;
         p.q = a->q;
         p.q_out = rope->q_out;
     }
-    const int grid = p.cache_wgs + (plan ? 1 : 0);
+    const int grid = p.cache_wgs + p.rope_wgs + (plan ? 1 : 0);
     if (grid == 0) return CPA_OK;
     if (rope)
         hipLaunchKernelGGL((prep_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, stream, p);

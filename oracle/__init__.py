@@ -20,6 +20,11 @@ Everything is written as the plain definition, in float64, from these pages:
 * "vLLM Chunked Prefill 如何改变 KV Cache 管理": incremental block
   allocation (section 2.1), block-aligned budget (section 2.3).
 
+``prefix_cache`` and the prefix-caching part of ``schedule`` follow the
+block hash chain, full-block matching and the pool's three buckets
+("Prefill Optimisation ...", sections 3 and 7) and the first-chunk-only
+lookup ("vLLM Chunked Prefill ...", sections 2.2 and 3.1).
+
 ``rope`` adds rotary position embedding at absolute positions ("Prefill
 Optimisation ...", section 2, "Causal equivalence"; "Chunked Prefill",
 section "From scratch"), in the standard rotary form, which the pages name
@@ -32,4 +37,4 @@ never define it); it is fixed to the consecutive grouping that
 ``torch.nn.functional.scaled_dot_product_attention`` uses and is pinned only
 against that library convention.
 """
-from . import attention, counters, rope, schedule  # noqa: F401
+from . import attention, counters, prefix_cache, rope, schedule  # noqa: F401

@@ -15,10 +15,24 @@ the batch descriptor.  Plain Python, integer work only.
   "vLLM Chunked Prefill ..." section 2.1 (incremental growth per chunk).
 * Shared prefix blocks carry a reference count ("Prefill Optimisation ...",
   section 3, "Three disjoint block buckets").
+* Prefix caching (optional): the pool's blocks fall in three disjoint
+  buckets, active (reference count > 0), reclaimable cached (count 0, still
+  holding a known full block) and empty ("Prefill Optimisation ...", section
+  3, "Cache granularity and eviction in preallocated pools"); the free count
+  includes the reclaimable ones (same section, "Accounting considerations").
+  Allocation takes empty blocks first and then evicts the least recently
+  freed cached block, unlinking its digest (eviction is host metadata only).
+  A request's prefix is looked up once, when it is first scheduled, and only
+  over the blocks of that first chunk ("vLLM Chunked Prefill ...", section
+  2.2 and the scenario of section 3.1); full blocks are registered under
+  their chained digest (``oracle.prefix_cache``) as their tokens are
+  computed.
 """
 from __future__ import annotations
 
-from collections import deque
+from collections import OrderedDict, deque
+
+from . import prefix_cache as _pc
 
 
 class BudgetExhausted(RuntimeError):
@@ -62,23 +76,45 @@ def schedule_prompt(max_batched_tokens: int, active_decodes: int, total_prompt_t
 
 
 class BlockPool:
-    """Fixed pool of physical blocks: a FIFO free list (in the given order)
-    and a reference count per block."""
+    """Fixed pool of physical blocks: a FIFO list of empty blocks (in the
+    given order), a reference count per block and, for prefix caching, the
+    digest a block holds, the digest table and the reclaimable cached blocks
+    in the order they were freed."""
 
     def __init__(self, num_blocks: int, free_order=None):
         order = range(num_blocks) if free_order is None else [int(x) for x in free_order]
         self.free = deque(order)
         self.ref = [0] * num_blocks
+        self.digest = [None] * num_blocks
+        self.table = {}
+        self.lru = OrderedDict()
 
     def num_free(self) -> int:
+        """Empty plus reclaimable blocks: what allocation can hand out."""
+        return len(self.free) + len(self.lru)
+
+    def num_empty(self) -> int:
         return len(self.free)
 
+    def num_reclaimable(self) -> int:
+        return len(self.lru)
+
+    def num_active(self) -> int:
+        return sum(1 for r in self.ref if r > 0)
+
     def allocate(self, n: int) -> list:
-        if n > len(self.free):
-            raise OutOfBlocks(f"need {n} blocks, {len(self.free)} free")
-        out = [self.free.popleft() for _ in range(n)]
-        for blk in out:
+        if n > self.num_free():
+            raise OutOfBlocks(f"need {n} blocks, {self.num_free()} free")
+        out = []
+        for _ in range(n):
+            if self.free:
+                blk = self.free.popleft()
+            else:
+                blk, _ = self.lru.popitem(last=False)     # least recently freed cached block
+                del self.table[self.digest[blk]]
+                self.digest[blk] = None
             self.ref[blk] = 1
+            out.append(blk)
         return out
 
     def share(self, blocks) -> None:
@@ -87,20 +123,56 @@ class BlockPool:
                 raise ValueError(f"block {blk} is not active")
             self.ref[blk] += 1
 
+    def claim(self, blk: int) -> None:
+        """A prefix hit: an active or a reclaimable cached block gains a user."""
+        if self.ref[blk] == 0:
+            del self.lru[blk]
+        self.ref[blk] += 1
+
+    def register(self, blk: int, digest: str) -> None:
+        """Block ``blk`` now holds the full block ``digest`` (first holder wins)."""
+        if digest not in self.table:
+            self.table[digest] = blk
+            self.digest[blk] = digest
+
+    def lookup(self, digests) -> list:
+        """Blocks of the longest run of known digests from the first."""
+        out = []
+        for d in digests:
+            if d not in self.table:
+                break
+            out.append(self.table[d])
+        return out
+
     def release(self, blocks) -> None:
+        """Drop one reference from each block.  Blocks left unused go back
+        empty, in order; cached ones become reclaimable, the sequence's last
+        block first, so that its leading blocks are evicted last."""
+        unused = []
         for blk in blocks:
             self.ref[blk] -= 1
             if self.ref[blk] == 0:
+                unused.append(blk)
+        for blk in unused:
+            if self.digest[blk] is None:
                 self.free.append(blk)
+        for blk in reversed(unused):
+            if self.digest[blk] is not None:
+                self.lru[blk] = None
 
 
 class Request:
-    def __init__(self, req_id: int, num_tokens: int, num_computed: int, blocks, is_decode: bool):
+    def __init__(self, req_id: int, num_tokens: int, num_computed: int, blocks, is_decode: bool,
+                 tokens=None, namespace: str = "default"):
         self.req_id = req_id
         self.num_tokens = num_tokens        # tokens known so far (prompt, then + generated)
         self.num_computed = num_computed    # tokens whose KV is in the cache
         self.blocks = list(blocks)
         self.is_decode = is_decode
+        self.tokens = None if tokens is None else [int(t) for t in tokens]   # prompt token ids
+        self.namespace = namespace
+        self.digests = []                   # chained digests of its first full blocks
+        self.looked_up = False
 
 
 class Scheduler:
@@ -108,7 +180,7 @@ class Scheduler:
 
     def __init__(self, pool: BlockPool, block_size: int, max_batched_tokens: int,
                  max_blocks_per_seq: int, long_prefill_cap: int = 0,
-                 align_to_block: bool = False):
+                 align_to_block: bool = False, prefix_caching: bool = False):
         if block_size <= 0 or max_batched_tokens <= 0 or max_blocks_per_seq <= 0:
             raise ValueError("block_size, max_batched_tokens, max_blocks_per_seq must be positive")
         self.pool = pool
@@ -117,6 +189,7 @@ class Scheduler:
         self.max_blocks = max_blocks_per_seq
         self.cap = long_prefill_cap
         self.align = align_to_block
+        self.prefix_caching = prefix_caching
         self.reqs = []      # FCFS order
 
     def _find(self, req_id):
@@ -140,6 +213,17 @@ class Scheduler:
         self.pool.share(prefix_blocks)
         self.reqs.append(Request(req_id, num_prompt_tokens, computed, prefix_blocks, False))
 
+    def add_request_tokens(self, req_id: int, tokens, namespace: str = "default"):
+        """A new prompt given by its token ids.  With prefix caching on, its
+        cached prefix is looked up when it is first scheduled, and its full
+        blocks are registered as they are computed."""
+        tokens = list(tokens)
+        if not tokens:
+            raise ValueError("empty prompt")
+        if cdiv(len(tokens), self.block_size) > self.max_blocks:
+            raise ValueError("prompt longer than a block-table row can map")
+        self.reqs.append(Request(req_id, len(tokens), 0, [], False, tokens, namespace))
+
     def add_partial(self, req_id: int, num_prompt_tokens: int, num_computed_tokens: int):
         """A prompt whose first ``num_computed_tokens`` are already cached in
         blocks it owns (taken from the pool now); prefill resumes there."""
@@ -160,11 +244,23 @@ class Scheduler:
         blocks = self.pool.allocate(cdiv(context_len, self.block_size))
         self.reqs.append(Request(req_id, context_len + 1, context_len, blocks, True))
 
+    def _take(self, remaining: int, used: int) -> int:
+        """Tokens a prefill with ``remaining`` left gets when ``used`` of the
+        budget is spoken for."""
+        take = min(remaining, self.budget - used)
+        if self.cap > 0:
+            take = min(take, self.cap)
+        if self.align and take < remaining:
+            take = (take // self.block_size) * self.block_size
+        return take
+
     def step(self) -> dict:
         """Pick this step's tokens, grow the block tables, return the batch
-        descriptor (decodes first, then prefills, each in arrival order)."""
+        descriptor (decodes first, then prefills, each in arrival order).
+        Nothing changes when the pool cannot hold the step."""
         used = 0
         picked = []
+        hits = {}           # request -> blocks of its prefix hit (first scheduling only)
         for r in self.reqs:
             if r.is_decode and used < self.budget:
                 picked.append((r, 1))
@@ -174,24 +270,48 @@ class Scheduler:
                 continue
             if used >= self.budget:
                 break
-            remaining = r.num_tokens - r.num_computed
-            take = min(remaining, self.budget - used)
-            if self.cap > 0:
-                take = min(take, self.cap)
-            if self.align and take < remaining:
-                take = (take // self.block_size) * self.block_size
+            computed = r.num_computed
+            hit = None
+            if (self.prefix_caching and r.tokens is not None and not r.looked_up
+                    and r.num_computed == 0):
+                # the lookup covers the full blocks of the first chunk only,
+                # and leaves at least the prompt's last token to compute
+                first = self._take(r.num_tokens, used)
+                limit = min(first, r.num_tokens - 1) // self.block_size
+                digests = _pc.chain(r.tokens[:limit * self.block_size], self.block_size,
+                                    r.namespace)
+                hit = self.pool.lookup(digests)
+                computed = len(hit) * self.block_size
+            take = self._take(r.num_tokens - computed, used)
             if take <= 0:
                 continue
+            if hit is not None:
+                hits[id(r)] = hit
             picked.append((r, take))
             used += take
         need_new = []
         for r, take in picked:
-            need = cdiv(r.num_computed + take, self.block_size)
+            hit = hits.get(id(r))
+            computed = r.num_computed if hit is None else len(hit) * self.block_size
+            held = len(r.blocks) if hit is None else len(hit)
+            need = cdiv(computed + take, self.block_size)
             if need > self.max_blocks:
                 raise ValueError(f"request {r.req_id} needs {need} blocks > row width {self.max_blocks}")
-            need_new.append(need - len(r.blocks))
-        if sum(need_new) > self.pool.num_free():
-            raise OutOfBlocks(f"step needs {sum(need_new)} blocks, {self.pool.num_free()} free")
+            need_new.append(need - held)
+        claimed = {b for h in hits.values() for b in h if self.pool.ref[b] == 0}
+        if sum(need_new) > self.pool.num_free() - len(claimed):
+            raise OutOfBlocks(f"step needs {sum(need_new)} blocks, "
+                              f"{self.pool.num_free() - len(claimed)} free")
+        for r, _ in picked:
+            hit = hits.get(id(r))
+            if hit is None:
+                continue
+            r.looked_up = True
+            for b in hit:
+                self.pool.claim(b)
+            r.blocks = list(hit)
+            r.num_computed = len(hit) * self.block_size
+            r.digests = _pc.chain(r.tokens[:r.num_computed], self.block_size, r.namespace)
         for (r, _), k in zip(picked, need_new):
             r.blocks.extend(self.pool.allocate(k))
         cu = [0]
@@ -215,12 +335,24 @@ class Scheduler:
         a decode of the token its last chunk produced."""
         for r, take in self._last:
             r.num_computed += take
+            if self.prefix_caching and r.tokens is not None:
+                self._register(r)
             if r.is_decode:
                 r.num_tokens += 1
             elif r.num_computed == r.num_tokens:
                 r.is_decode = True
                 r.num_tokens += 1
         self._last = []
+
+    def _register(self, r) -> None:
+        """Register the request's newly full prompt blocks under their digests."""
+        bs = self.block_size
+        full = min(r.num_computed, len(r.tokens)) // bs
+        for j in range(len(r.digests), full):
+            parent = r.digests[-1] if r.digests else _pc.ROOT
+            d = _pc.block_hash(parent, r.tokens[j * bs:(j + 1) * bs], r.namespace)
+            self.pool.register(r.blocks[j], d)
+            r.digests.append(d)
 
     def free_request(self, req_id: int) -> None:
         r = self._find(req_id)

@@ -58,7 +58,7 @@ class PlanInfo(ctypes.Structure):
 class SchedConfig(ctypes.Structure):
     _fields_ = [("num_blocks", _i32), ("block_size", _i32), ("max_batched_tokens", _i32),
                 ("max_blocks_per_seq", _i32), ("long_prefill_cap", _i32),
-                ("align_to_block", _i32), ("free_order", _p_i32)]
+                ("align_to_block", _i32), ("free_order", _p_i32), ("prefix_caching", _i32)]
 
 
 class Batch(ctypes.Structure):
@@ -86,6 +86,8 @@ SIGNATURES = {
     "cpa_sched_create": (ctypes.c_int, [ctypes.POINTER(SchedConfig), ctypes.POINTER(_vp)]),
     "cpa_sched_destroy": (None, [_vp]),
     "cpa_sched_add_request": (ctypes.c_int, [_vp, _i64, _i32, _p_i32, _i32]),
+    "cpa_sched_add_request_tokens": (ctypes.c_int, [_vp, _i64, ctypes.POINTER(ctypes.c_uint32), _i32,
+                                                    ctypes.c_char_p]),
     "cpa_sched_add_decode": (ctypes.c_int, [_vp, _i64, _i32]),
     "cpa_sched_add_partial": (ctypes.c_int, [_vp, _i64, _i32, _i32]),
     "cpa_sched_step": (ctypes.c_int, [_vp, ctypes.POINTER(Batch)]),
@@ -96,6 +98,9 @@ SIGNATURES = {
     "cpa_sched_slots": (ctypes.c_int, [_vp, _i64, _i32, _i32, _p_i64]),
     "cpa_sched_num_free_blocks": (ctypes.c_int, [_vp, _p_i32]),
     "cpa_sched_block_refcount": (ctypes.c_int, [_vp, _i32, _p_i32]),
+    "cpa_sched_pool_stats": (ctypes.c_int, [_vp, _p_i32, _p_i32, _p_i32]),
+    "cpa_sched_prefix_match": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_uint32), _i32,
+                                              ctypes.c_char_p, _p_i32]),
 }
 
 

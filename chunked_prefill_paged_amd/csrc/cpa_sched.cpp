@@ -9,10 +9,25 @@
 // prefix hits, block-aligned budget); "Prefill Processing", sections
 // "Scheduler Integration" and "Block Allocation".
 
+//
+// Prefix caching (optional): "Prefill Optimisation ...", section 3 ("vLLM
+// block hash chain": a full block is identified by its parent's digest, the
+// scope and its ordered token ids; full-block-only reuse; "Cache granularity
+// and eviction in preallocated pools": active, reclaimable cached and empty
+// blocks, the free count including reclaimable ones, eviction as host
+// metadata) and "vLLM Chunked Prefill ...", sections 2.2 and 3.1 (the
+// lookup happens once, at a request's first scheduling, over its first
+// chunk).  Digests here are 64-bit; every hit is verified against the
+// block's stored parent digest, scope and tokens, so a digest collision can
+// only cost a miss, never a wrong reuse.
+
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <deque>
+#include <list>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "chunked_prefill_attn.h"
@@ -21,12 +36,51 @@ namespace {
 
 inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+inline uint64_t mix64(uint64_t x) {
+    x ^= x >> 30;
+    x *= 0xbf58476d1ce4e5b9ULL;
+    x ^= x >> 27;
+    x *= 0x94d049bb133111ebULL;
+    x ^= x >> 31;
+    return x;
+}
+
+// digest of a full block from its parent's digest (0 for the first block),
+// the scope digest and its token ids
+uint64_t block_digest(uint64_t parent, uint64_t scope, const uint32_t* tok, int32_t n) {
+    uint64_t h = mix64(parent + 0x9e3779b97f4a7c15ULL);
+    h = mix64(h ^ scope);
+    for (int32_t i = 0; i < n; ++i) h = mix64(h ^ ((uint64_t)tok[i] | ((uint64_t)(i + 1) << 32)));
+    return h | 1;   // never 0, the "no parent" value
+}
+
+// FNV-1a over the scope name
+uint64_t scope_digest(const char* name) {
+    uint64_t h = 0xcbf29ce484222325ULL;
+    for (const char* c = name ? name : "default"; *c; ++c) {
+        h ^= (unsigned char)*c;
+        h *= 0x100000001b3ULL;
+    }
+    return h;
+}
+
 struct Request {
     int64_t id;
     int32_t num_tokens;    // tokens known (prompt, then + generated)
     int32_t num_computed;  // tokens whose KV is cached
     bool is_decode;
     std::vector<int32_t> blocks;
+    // prefix caching
+    std::vector<uint32_t> tokens;    // prompt token ids (empty: not given)
+    uint64_t scope = 0;
+    std::vector<uint64_t> digests;   // chained digests of its first full blocks
+    bool looked_up = false;
+};
+
+// identity of a registered block, for verifying a digest hit
+struct BlockKey {
+    uint64_t parent = 0, scope = 0;
+    std::vector<uint32_t> tokens;
 };
 
 }  // namespace
@@ -37,10 +91,18 @@ struct cpa_sched {
     int32_t max_blocks = 0;
     int32_t cap = 0;
     bool align = false;
-    std::deque<int32_t> free_list;      // FIFO: hand out from the front
+    bool caching = false;
+    std::deque<int32_t> free_list;      // empty blocks, FIFO: hand out from the front
     std::vector<int32_t> ref;           // reference count per block
     std::vector<Request> reqs;          // arrival order
     std::vector<std::pair<size_t, int32_t>> last;  // (request index, tokens) of the last step
+    // prefix caching: digest held by each block (0: none), the digest table,
+    // reclaimable cached blocks oldest first
+    std::vector<uint64_t> digest;
+    std::vector<BlockKey> key;
+    std::unordered_map<uint64_t, int32_t> table;
+    std::list<int32_t> lru;
+    std::vector<std::list<int32_t>::iterator> lru_pos;
 
     Request* find(int64_t id) {
         for (auto& r : reqs)
@@ -52,18 +114,84 @@ struct cpa_sched {
             if (r.id == id) return &r;
         return nullptr;
     }
+    int64_t num_free() const { return (int64_t)free_list.size() + (int64_t)lru.size(); }
+    // empty blocks first, then the least recently freed cached block
     void take(int32_t n, std::vector<int32_t>& dst) {
         for (int32_t i = 0; i < n; ++i) {
-            int32_t b = free_list.front();
-            free_list.pop_front();
+            int32_t b;
+            if (!free_list.empty()) {
+                b = free_list.front();
+                free_list.pop_front();
+            } else {
+                b = lru.front();
+                lru.pop_front();
+                table.erase(digest[b]);
+                digest[b] = 0;
+                key[b] = BlockKey();
+            }
             ref[b] = 1;
             dst.push_back(b);
         }
     }
+    // blocks left unused go back empty in order; cached ones become
+    // reclaimable, the sequence's last block first
     void release(const std::vector<int32_t>& blocks) {
-        for (int32_t b : blocks) {
-            if (--ref[b] == 0) free_list.push_back(b);
+        std::vector<int32_t> unused;
+        for (int32_t b : blocks)
+            if (--ref[b] == 0) unused.push_back(b);
+        for (int32_t b : unused)
+            if (!digest[b]) free_list.push_back(b);
+        for (auto it = unused.rbegin(); it != unused.rend(); ++it)
+            if (digest[*it]) lru_pos[*it] = lru.insert(lru.end(), *it);
+    }
+    void claim(int32_t b) {
+        if (ref[b] == 0) lru.erase(lru_pos[b]);
+        ref[b] += 1;
+    }
+    // blocks of the longest run of the first nblk full blocks of `tok` that
+    // are registered (digests in `dig`)
+    void lookup(const std::vector<uint32_t>& tok, uint64_t scope, int32_t nblk,
+                std::vector<int32_t>& hit, std::vector<uint64_t>& dig) const {
+        uint64_t parent = 0;
+        for (int32_t j = 0; j < nblk; ++j) {
+            const uint32_t* t = tok.data() + (size_t)j * block_size;
+            const uint64_t d = block_digest(parent, scope, t, block_size);
+            auto f = table.find(d);
+            if (f == table.end()) break;
+            const BlockKey& k = key[f->second];
+            if (k.parent != parent || k.scope != scope ||
+                std::memcmp(k.tokens.data(), t, sizeof(uint32_t) * block_size) != 0)
+                break;
+            hit.push_back(f->second);
+            dig.push_back(d);
+            parent = d;
         }
+    }
+    // register the request's newly full prompt blocks (first holder wins)
+    void register_blocks(Request& r) {
+        const int64_t known = (int64_t)r.tokens.size();
+        const int64_t full = (r.num_computed < known ? r.num_computed : known) / block_size;
+        for (int64_t j = (int64_t)r.digests.size(); j < full; ++j) {
+            const uint64_t parent = r.digests.empty() ? 0 : r.digests.back();
+            const uint32_t* t = r.tokens.data() + (size_t)j * block_size;
+            const uint64_t d = block_digest(parent, r.scope, t, block_size);
+            const int32_t b = r.blocks[(size_t)j];
+            if (!table.count(d)) {
+                table[d] = b;
+                digest[b] = d;
+                key[b].parent = parent;
+                key[b].scope = r.scope;
+                key[b].tokens.assign(t, t + block_size);
+            }
+            r.digests.push_back(d);
+        }
+    }
+    // tokens a prefill with `remaining` left gets when `used` of the budget is taken
+    int64_t take_for(int64_t remaining, int64_t used) const {
+        int64_t t = remaining < budget - used ? remaining : budget - used;
+        if (cap > 0 && t > cap) t = cap;
+        if (align && t < remaining) t = (t / block_size) * block_size;
+        return t;
     }
 };
 
@@ -108,7 +236,11 @@ cpa_status cpa_sched_create(const cpa_sched_config* cfg, cpa_sched** out) {
     s->max_blocks = cfg->max_blocks_per_seq;
     s->cap = cfg->long_prefill_cap;
     s->align = cfg->align_to_block != 0;
+    s->caching = cfg->prefix_caching != 0;
     s->ref.assign(cfg->num_blocks, 0);
+    s->digest.assign(cfg->num_blocks, 0);
+    s->key.resize(cfg->num_blocks);
+    s->lru_pos.resize(cfg->num_blocks);
     if (cfg->free_order) {
         std::vector<char> seen(cfg->num_blocks, 0);
         for (int32_t i = 0; i < cfg->num_blocks; ++i) {
@@ -154,12 +286,28 @@ cpa_status cpa_sched_add_request(cpa_sched* s, int64_t req_id, int32_t num_promp
     return CPA_OK;
 }
 
+cpa_status cpa_sched_add_request_tokens(cpa_sched* s, int64_t req_id, const uint32_t* tokens,
+                                        int32_t num_tokens, const char* name_space) {
+    if (!s || num_tokens <= 0 || !tokens) return CPA_ERR_INVALID_ARG;
+    if (s->find(req_id)) return CPA_ERR_INVALID_ARG;
+    if (cdiv64(num_tokens, s->block_size) > s->max_blocks) return CPA_ERR_INVALID_ARG;
+    Request r;
+    r.id = req_id;
+    r.num_tokens = num_tokens;
+    r.num_computed = 0;
+    r.is_decode = false;
+    r.tokens.assign(tokens, tokens + num_tokens);
+    r.scope = scope_digest(name_space);
+    s->reqs.push_back(std::move(r));
+    return CPA_OK;
+}
+
 cpa_status cpa_sched_add_decode(cpa_sched* s, int64_t req_id, int32_t context_len) {
     if (!s || context_len <= 0) return CPA_ERR_INVALID_ARG;
     if (s->find(req_id)) return CPA_ERR_INVALID_ARG;
     const int64_t need = cdiv64(context_len, s->block_size);
     if (cdiv64((int64_t)context_len + 1, s->block_size) > s->max_blocks) return CPA_ERR_INVALID_ARG;
-    if (need > (int64_t)s->free_list.size()) return CPA_ERR_OUT_OF_BLOCKS;
+    if (need > s->num_free()) return CPA_ERR_OUT_OF_BLOCKS;
     Request r;
     r.id = req_id;
     r.num_tokens = context_len + 1;
@@ -177,7 +325,7 @@ cpa_status cpa_sched_add_partial(cpa_sched* s, int64_t req_id, int32_t num_promp
     if (s->find(req_id)) return CPA_ERR_INVALID_ARG;
     if (cdiv64(num_prompt_tokens, s->block_size) > s->max_blocks) return CPA_ERR_INVALID_ARG;
     const int64_t need = cdiv64(num_computed_tokens, s->block_size);
-    if (need > (int64_t)s->free_list.size()) return CPA_ERR_OUT_OF_BLOCKS;
+    if (need > s->num_free()) return CPA_ERR_OUT_OF_BLOCKS;
     Request r;
     r.id = req_id;
     r.num_tokens = num_prompt_tokens;
@@ -199,16 +347,36 @@ cpa_status cpa_sched_step(cpa_sched* s, cpa_batch* out) {
             used += 1;
         }
     }
-    // then prefills in arrival order with what is left
+    // then prefills in arrival order with what is left; a request seen for
+    // the first time looks its prefix up over its first chunk (the hit
+    // leaves at least the prompt's last token to compute)
+    struct Hit {
+        std::vector<int32_t> blocks;
+        std::vector<uint64_t> digests;
+    };
+    std::vector<int32_t> hit_of(s->reqs.size(), -1);
+    std::vector<Hit> hits;
     for (size_t i = 0; i < s->reqs.size(); ++i) {
         const Request& r = s->reqs[i];
         if (r.is_decode) continue;
         if (used >= s->budget) break;
-        const int64_t remaining = (int64_t)r.num_tokens - r.num_computed;
-        int64_t take = remaining < s->budget - used ? remaining : s->budget - used;
-        if (s->cap > 0 && take > s->cap) take = s->cap;
-        if (s->align && take < remaining) take = (take / s->block_size) * s->block_size;
+        int64_t computed = r.num_computed;
+        bool look = false;
+        Hit h;
+        if (s->caching && !r.tokens.empty() && !r.looked_up && r.num_computed == 0) {
+            const int64_t first = s->take_for(r.num_tokens, used);
+            const int64_t lim = first < r.num_tokens - 1 ? first : r.num_tokens - 1;
+            s->lookup(r.tokens, r.scope, (int32_t)(lim > 0 ? lim / s->block_size : 0), h.blocks,
+                      h.digests);
+            computed = (int64_t)h.blocks.size() * s->block_size;
+            look = true;
+        }
+        const int64_t take = s->take_for((int64_t)r.num_tokens - computed, used);
         if (take <= 0) continue;
+        if (look) {
+            hit_of[i] = (int32_t)hits.size();
+            hits.push_back(std::move(h));
+        }
         picked.emplace_back(i, (int32_t)take);
         used += take;
     }
@@ -217,17 +385,37 @@ cpa_status cpa_sched_step(cpa_sched* s, cpa_batch* out) {
     if (!out->req_ids || !out->q_lens || !out->cu_seqlens_q || !out->cached_seq_len ||
         !out->block_table || !out->slot_mapping)
         return CPA_ERR_INVALID_ARG;
-    // block growth: all or nothing
+    // block growth: all or nothing (prefix hits on reclaimable blocks take
+    // them out of the free count)
     int64_t need_total = 0;
     std::vector<int32_t> need_new(picked.size());
+    std::vector<int32_t> claimed;
     for (size_t k = 0; k < picked.size(); ++k) {
         const Request& r = s->reqs[picked[k].first];
-        const int64_t need = cdiv64((int64_t)r.num_computed + picked[k].second, s->block_size);
+        const int32_t hi = hit_of[picked[k].first];
+        const int64_t computed = hi < 0 ? r.num_computed : (int64_t)hits[hi].blocks.size() * s->block_size;
+        const int64_t held = hi < 0 ? (int64_t)r.blocks.size() : (int64_t)hits[hi].blocks.size();
+        const int64_t need = cdiv64(computed + picked[k].second, s->block_size);
         if (need > s->max_blocks) return CPA_ERR_INVALID_ARG;
-        need_new[k] = (int32_t)(need - (int64_t)r.blocks.size());
+        need_new[k] = (int32_t)(need - held);
         need_total += need_new[k];
+        if (hi >= 0)
+            for (int32_t b : hits[hi].blocks)
+                if (s->ref[b] == 0) claimed.push_back(b);
     }
-    if (need_total > (int64_t)s->free_list.size()) return CPA_ERR_OUT_OF_BLOCKS;
+    std::sort(claimed.begin(), claimed.end());
+    claimed.erase(std::unique(claimed.begin(), claimed.end()), claimed.end());
+    if (need_total > s->num_free() - (int64_t)claimed.size()) return CPA_ERR_OUT_OF_BLOCKS;
+    for (size_t k = 0; k < picked.size(); ++k) {
+        const int32_t hi = hit_of[picked[k].first];
+        if (hi < 0) continue;
+        Request& r = s->reqs[picked[k].first];
+        r.looked_up = true;
+        for (int32_t b : hits[hi].blocks) s->claim(b);
+        r.blocks = hits[hi].blocks;
+        r.num_computed = (int32_t)(r.blocks.size() * (size_t)s->block_size);
+        r.digests = hits[hi].digests;
+    }
     for (size_t k = 0; k < picked.size(); ++k) {
         Request& r = s->reqs[picked[k].first];
         if (need_new[k] > 0) s->take(need_new[k], r.blocks);
@@ -262,6 +450,7 @@ cpa_status cpa_sched_commit(cpa_sched* s) {
     for (auto& pk : s->last) {
         Request& r = s->reqs[pk.first];
         r.num_computed += pk.second;
+        if (s->caching && !r.tokens.empty()) s->register_blocks(r);
         if (r.is_decode) {
             r.num_tokens += 1;
         } else if (r.num_computed == r.num_tokens) {
@@ -325,7 +514,30 @@ cpa_status cpa_sched_slots(const cpa_sched* s, int64_t req_id, int32_t pos0, int
 
 cpa_status cpa_sched_num_free_blocks(const cpa_sched* s, int32_t* num_free) {
     if (!s || !num_free) return CPA_ERR_INVALID_ARG;
-    *num_free = (int32_t)s->free_list.size();
+    *num_free = (int32_t)s->num_free();
+    return CPA_OK;
+}
+
+cpa_status cpa_sched_pool_stats(const cpa_sched* s, int32_t* num_active, int32_t* num_reclaimable,
+                                int32_t* num_empty) {
+    if (!s) return CPA_ERR_INVALID_ARG;
+    int32_t active = 0;
+    for (int32_t r : s->ref) active += r > 0;
+    if (num_active) *num_active = active;
+    if (num_reclaimable) *num_reclaimable = (int32_t)s->lru.size();
+    if (num_empty) *num_empty = (int32_t)s->free_list.size();
+    return CPA_OK;
+}
+
+cpa_status cpa_sched_prefix_match(const cpa_sched* s, const uint32_t* tokens, int32_t num_tokens,
+                                  const char* name_space, int32_t* num_cached_tokens) {
+    if (!s || num_tokens < 0 || (num_tokens > 0 && !tokens) || !num_cached_tokens)
+        return CPA_ERR_INVALID_ARG;
+    std::vector<uint32_t> tok(tokens, tokens + num_tokens);
+    std::vector<int32_t> hit;
+    std::vector<uint64_t> dig;
+    s->lookup(tok, scope_digest(name_space), num_tokens / s->block_size, hit, dig);
+    *num_cached_tokens = (int32_t)(hit.size() * (size_t)s->block_size);
     return CPA_OK;
 }
 

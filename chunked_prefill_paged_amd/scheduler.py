@@ -33,7 +33,7 @@ class HostScheduler:
 
     def __init__(self, num_blocks: int, block_size: int, max_batched_tokens: int,
                  max_blocks_per_seq: int, long_prefill_cap: int = 0, align_to_block: bool = False,
-                 free_order=None):
+                 free_order=None, prefix_caching: bool = False):
         self.block_size = block_size
         self.max_blocks = max_blocks_per_seq
         self.budget = max_batched_tokens
@@ -44,6 +44,7 @@ class HostScheduler:
         cfg.max_blocks_per_seq = max_blocks_per_seq
         cfg.long_prefill_cap = long_prefill_cap
         cfg.align_to_block = int(bool(align_to_block))
+        cfg.prefix_caching = int(bool(prefix_caching))
         self._order = None
         if free_order is not None:
             self._order = np.ascontiguousarray(free_order, dtype=np.int32)
@@ -65,6 +66,15 @@ class HostScheduler:
         _lib.check(_lib.lib().cpa_sched_add_request(self._h, req_id, num_prompt_tokens,
                                                     _i32p(blocks), len(blocks)),
                    "cpa_sched_add_request")
+        self._max_seqs += 1
+
+    def add_request_tokens(self, req_id: int, tokens, namespace: str = "default"):
+        """A prompt given by its token ids (prefix caching matches and
+        registers its full blocks)."""
+        t = np.ascontiguousarray(tokens, dtype=np.uint32)
+        _lib.check(_lib.lib().cpa_sched_add_request_tokens(
+            self._h, req_id, t.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), len(t),
+            namespace.encode("utf-8")), "cpa_sched_add_request_tokens")
         self._max_seqs += 1
 
     def add_decode(self, req_id: int, context_len: int):
@@ -132,6 +142,21 @@ class HostScheduler:
         _lib.check(_lib.lib().cpa_sched_num_free_blocks(self._h, ctypes.byref(v)),
                    "cpa_sched_num_free_blocks")
         return v.value
+
+    def pool_stats(self) -> dict:
+        v = [ctypes.c_int32() for _ in range(3)]
+        _lib.check(_lib.lib().cpa_sched_pool_stats(self._h, *(ctypes.byref(x) for x in v)),
+                   "cpa_sched_pool_stats")
+        return {"active": v[0].value, "reclaimable": v[1].value, "empty": v[2].value}
+
+    def prefix_match(self, tokens, namespace: str = "default") -> int:
+        """Cached tokens (whole blocks) a prompt would match now."""
+        t = np.ascontiguousarray(tokens, dtype=np.uint32)
+        n = ctypes.c_int32()
+        _lib.check(_lib.lib().cpa_sched_prefix_match(
+            self._h, t.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), len(t),
+            namespace.encode("utf-8"), ctypes.byref(n)), "cpa_sched_prefix_match")
+        return n.value
 
     def refcount(self, block: int) -> int:
         v = ctypes.c_int32()

@@ -245,6 +245,8 @@ typedef struct cpa_sched_config {
     const int32_t* free_order;   /* host [num_blocks]: order in which free
                                     blocks are handed out (a permutation of
                                     0..num_blocks-1), NULL = 0,1,2,...         */
+    int32_t prefix_caching;      /* 1: match and register full prompt blocks
+                                    of requests given by token ids (below)    */
 } cpa_sched_config;
 
 /* Batch descriptor of one step, written into caller-owned host arrays. */
@@ -271,6 +273,26 @@ void       cpa_sched_destroy(cpa_sched* sched);
  * section 2.2).  Every prefix block must be active (held by someone). */
 cpa_status cpa_sched_add_request(cpa_sched* sched, int64_t req_id, int32_t num_prompt_tokens,
                                  const int32_t* prefix_blocks, int32_t num_prefix_blocks);
+
+/* New prompt given by its token ids under a scope (name_space; NULL means
+ * "default").  With prefix_caching on ("Prefill Optimisation ...", section
+ * 3, "vLLM block hash chain"; "vLLM Chunked Prefill ...", sections 2.2 and
+ * 3.1):
+ *   - when the request is first scheduled, its prompt's full blocks are
+ *     looked up along the parent-chained digest of (parent, scope, token
+ *     ids), over the blocks of that first chunk only and leaving at least the
+ *     prompt's last token to compute; the matched blocks join its table with
+ *     their reference counts raised and count as computed;
+ *   - each full prompt block it computes is registered under its digest
+ *     (the first block holding a digest keeps it);
+ *   - blocks it releases that hold a registered digest become reclaimable
+ *     (its last block first) and are evicted, least recently freed first,
+ *     only when no empty block is left.
+ * Without prefix caching it behaves as cpa_sched_add_request with no
+ * prefix.  CPA_ERR_INVALID_ARG for an empty prompt, a duplicate id or a
+ * prompt longer than a table row maps. */
+cpa_status cpa_sched_add_request_tokens(cpa_sched* sched, int64_t req_id, const uint32_t* tokens,
+                                        int32_t num_tokens, const char* name_space);
 
 /* Running sequence with context_len cached tokens and one token to decode;
  * its cdiv(context_len, block_size) cache blocks are taken from the pool. */
@@ -302,7 +324,18 @@ cpa_status cpa_sched_request_blocks(const cpa_sched* sched, int64_t req_id, int3
  * held blocks). */
 cpa_status cpa_sched_slots(const cpa_sched* sched, int64_t req_id, int32_t pos0, int32_t n,
                            int64_t* slots);
+/* Blocks allocation can hand out: empty plus reclaimable cached ones
+ * ("Prefill Optimisation ...", section 3, "Accounting considerations"). */
 cpa_status cpa_sched_num_free_blocks(const cpa_sched* sched, int32_t* num_free);
+/* The pool's three disjoint buckets: active (reference count > 0),
+ * reclaimable cached (count 0, registered digest) and empty (any may be
+ * NULL). */
+cpa_status cpa_sched_pool_stats(const cpa_sched* sched, int32_t* num_active,
+                                int32_t* num_reclaimable, int32_t* num_empty);
+/* Tokens of `tokens` (full blocks from the first) that are registered now
+ * under name_space; no state changes. */
+cpa_status cpa_sched_prefix_match(const cpa_sched* sched, const uint32_t* tokens, int32_t num_tokens,
+                                  const char* name_space, int32_t* num_cached_tokens);
 cpa_status cpa_sched_block_refcount(const cpa_sched* sched, int32_t block, int32_t* refcount);
 
 #ifdef __cplusplus

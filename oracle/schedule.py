@@ -180,7 +180,8 @@ class Scheduler:
 
     def __init__(self, pool: BlockPool, block_size: int, max_batched_tokens: int,
                  max_blocks_per_seq: int, long_prefill_cap: int = 0,
-                 align_to_block: bool = False, prefix_caching: bool = False):
+                 align_to_block: bool = False, prefix_caching: bool = False,
+                 max_long_partial_prefills: int = 0, preemption: bool = False):
         if block_size <= 0 or max_batched_tokens <= 0 or max_blocks_per_seq <= 0:
             raise ValueError("block_size, max_batched_tokens, max_blocks_per_seq must be positive")
         self.pool = pool
@@ -190,6 +191,9 @@ class Scheduler:
         self.cap = long_prefill_cap
         self.align = align_to_block
         self.prefix_caching = prefix_caching
+        self.max_long = max_long_partial_prefills
+        self.preemption = preemption
+        self.preempted = []
         self.reqs = []      # FCFS order
 
     def _find(self, req_id):
@@ -254,22 +258,27 @@ class Scheduler:
             take = (take // self.block_size) * self.block_size
         return take
 
-    def step(self) -> dict:
-        """Pick this step's tokens, grow the block tables, return the batch
-        descriptor (decodes first, then prefills, each in arrival order).
-        Nothing changes when the pool cannot hold the step."""
+    def _plan(self, skip):
+        """This step's picks: (request, tokens) pairs, prefix hits and new
+        blocks per pick; requests in ``skip`` (preempted this step) wait."""
         used = 0
         picked = []
         hits = {}           # request -> blocks of its prefix hit (first scheduling only)
         for r in self.reqs:
-            if r.is_decode and used < self.budget:
+            if r.is_decode and used < self.budget and id(r) not in skip:
                 picked.append((r, 1))
                 used += 1
+        longs = 0
         for r in self.reqs:
-            if r.is_decode:
+            if r.is_decode or id(r) in skip:
                 continue
             if used >= self.budget:
                 break
+            # long prompts (longer than the per-prefill cap) beyond the
+            # allowed number per step wait; shorter ones behind them go on
+            is_long = self.cap > 0 and r.num_tokens > self.cap
+            if is_long and self.max_long > 0 and longs >= self.max_long:
+                continue
             computed = r.num_computed
             hit = None
             if (self.prefix_caching and r.tokens is not None and not r.looked_up
@@ -289,6 +298,7 @@ class Scheduler:
                 hits[id(r)] = hit
             picked.append((r, take))
             used += take
+            longs += is_long
         need_new = []
         for r, take in picked:
             hit = hits.get(id(r))
@@ -299,9 +309,45 @@ class Scheduler:
                 raise ValueError(f"request {r.req_id} needs {need} blocks > row width {self.max_blocks}")
             need_new.append(need - held)
         claimed = {b for h in hits.values() for b in h if self.pool.ref[b] == 0}
-        if sum(need_new) > self.pool.num_free() - len(claimed):
-            raise OutOfBlocks(f"step needs {sum(need_new)} blocks, "
-                              f"{self.pool.num_free() - len(claimed)} free")
+        fits = sum(need_new) <= self.pool.num_free() - len(claimed)
+        return picked, hits, need_new, used, fits, sum(need_new), len(claimed)
+
+    def _victim(self, skip):
+        """First-come-first-served: the most recently arrived request that
+        holds blocks ("vLLM Chunked Prefill ...", section 4)."""
+        holders = [r for r in self.reqs if r.blocks and id(r) not in skip]
+        return holders[-1] if holders else None
+
+    def _preempt(self, r) -> None:
+        """Release every block of ``r`` and send it back to position 0: it
+        recomputes all its known tokens (and looks its prefix up again)."""
+        self.pool.release(r.blocks)
+        r.blocks = []
+        r.num_computed = 0
+        r.is_decode = False
+        r.looked_up = False
+        r.digests = []
+
+    def step(self) -> dict:
+        """Pick this step's tokens, grow the block tables, return the batch
+        descriptor (decodes first, then prefills, each in arrival order).
+        When the pool cannot hold the step: without preemption nothing
+        changes and OutOfBlocks is raised; with it, the most recently
+        arrived request holding blocks is preempted (all its blocks freed,
+        its progress reset) and the step planned again, until it fits."""
+        skip = set()
+        self.preempted = []
+        while True:
+            picked, hits, need_new, used, fits, need, claimed = self._plan(skip)
+            if fits:
+                break
+            victim = self._victim(skip) if self.preemption else None
+            if victim is None:
+                raise OutOfBlocks(f"step needs {need} blocks, "
+                                  f"{self.pool.num_free() - claimed} free")
+            self._preempt(victim)
+            skip.add(id(victim))
+            self.preempted.append(victim.req_id)
         for r, _ in picked:
             hit = hits.get(id(r))
             if hit is None:

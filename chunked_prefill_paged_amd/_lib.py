@@ -58,7 +58,8 @@ class PlanInfo(ctypes.Structure):
 class SchedConfig(ctypes.Structure):
     _fields_ = [("num_blocks", _i32), ("block_size", _i32), ("max_batched_tokens", _i32),
                 ("max_blocks_per_seq", _i32), ("long_prefill_cap", _i32),
-                ("align_to_block", _i32), ("free_order", _p_i32), ("prefix_caching", _i32)]
+                ("align_to_block", _i32), ("free_order", _p_i32), ("prefix_caching", _i32),
+                ("max_long_partial_prefills", _i32), ("preemption", _i32)]
 
 
 class Batch(ctypes.Structure):
@@ -92,6 +93,7 @@ SIGNATURES = {
     "cpa_sched_add_partial": (ctypes.c_int, [_vp, _i64, _i32, _i32]),
     "cpa_sched_step": (ctypes.c_int, [_vp, ctypes.POINTER(Batch)]),
     "cpa_sched_commit": (ctypes.c_int, [_vp]),
+    "cpa_sched_last_preempted": (ctypes.c_int, [_vp, _p_i64, _i32, _p_i32]),
     "cpa_sched_free_request": (ctypes.c_int, [_vp, _i64]),
     "cpa_sched_request_info": (ctypes.c_int, [_vp, _i64, _p_i32, _p_i32, _p_i32, _p_i32]),
     "cpa_sched_request_blocks": (ctypes.c_int, [_vp, _i64, _p_i32, _i32, _p_i32]),

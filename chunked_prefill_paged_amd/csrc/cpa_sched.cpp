@@ -103,6 +103,10 @@ struct cpa_sched {
     std::unordered_map<uint64_t, int32_t> table;
     std::list<int32_t> lru;
     std::vector<std::list<int32_t>::iterator> lru_pos;
+    // long prompts per step and preemption
+    int32_t max_long = 0;
+    bool preemption = false;
+    std::vector<int64_t> preempted;     // ids preempted by the last step
 
     Request* find(int64_t id) {
         for (auto& r : reqs)
@@ -143,6 +147,16 @@ struct cpa_sched {
             if (!digest[b]) free_list.push_back(b);
         for (auto it = unused.rbegin(); it != unused.rend(); ++it)
             if (digest[*it]) lru_pos[*it] = lru.insert(lru.end(), *it);
+    }
+    // release every block of r and send it back to position 0: it recomputes
+    // all its known tokens (and looks its prefix up again)
+    void preempt(Request& r) {
+        release(r.blocks);
+        r.blocks.clear();
+        r.num_computed = 0;
+        r.is_decode = false;
+        r.looked_up = false;
+        r.digests.clear();
     }
     void claim(int32_t b) {
         if (ref[b] == 0) lru.erase(lru_pos[b]);
@@ -237,6 +251,12 @@ cpa_status cpa_sched_create(const cpa_sched_config* cfg, cpa_sched** out) {
     s->cap = cfg->long_prefill_cap;
     s->align = cfg->align_to_block != 0;
     s->caching = cfg->prefix_caching != 0;
+    if (cfg->max_long_partial_prefills < 0) {
+        delete s;
+        return CPA_ERR_INVALID_ARG;
+    }
+    s->max_long = cfg->max_long_partial_prefills;
+    s->preemption = cfg->preemption != 0;
     s->ref.assign(cfg->num_blocks, 0);
     s->digest.assign(cfg->num_blocks, 0);
     s->key.resize(cfg->num_blocks);
@@ -336,89 +356,138 @@ cpa_status cpa_sched_add_partial(cpa_sched* s, int64_t req_id, int32_t num_promp
     return CPA_OK;
 }
 
-cpa_status cpa_sched_step(cpa_sched* s, cpa_batch* out) {
-    if (!s || !out) return CPA_ERR_INVALID_ARG;
-    std::vector<std::pair<size_t, int32_t>> picked;
-    int64_t used = 0;
-    // decodes first, one token each
-    for (size_t i = 0; i < s->reqs.size(); ++i) {
-        if (s->reqs[i].is_decode && used < s->budget) {
-            picked.emplace_back(i, 1);
-            used += 1;
-        }
-    }
-    // then prefills in arrival order with what is left; a request seen for
-    // the first time looks its prefix up over its first chunk (the hit
-    // leaves at least the prompt's last token to compute)
+}  // extern "C"
+
+namespace {
+
+// One step's picks before anything changes: (request index, tokens), the
+// prefix hits of requests seen for the first time, and the new blocks each
+// pick needs.
+struct StepPlan {
     struct Hit {
         std::vector<int32_t> blocks;
         std::vector<uint64_t> digests;
     };
-    std::vector<int32_t> hit_of(s->reqs.size(), -1);
+    std::vector<std::pair<size_t, int32_t>> picked;
+    std::vector<int32_t> hit_of;   // per request: index into hits, -1 none
     std::vector<Hit> hits;
+    std::vector<int32_t> need_new;
+    int64_t used = 0, need_total = 0, claimed = 0;
+    bool too_wide = false;         // a table row cannot map a pick
+};
+
+// Decodes first, one token each; then prefills in arrival order with what is
+// left.  A prefill seen for the first time looks its prefix up over its first
+// chunk (leaving at least the prompt's last token to compute).  Prompts longer
+// than the per-prefill cap beyond max_long in a step wait; shorter ones behind
+// them go on.  Requests marked in `skip` (preempted this step) wait.
+void plan_step(const cpa_sched* s, const std::vector<char>& skip, StepPlan& p) {
+    p.hit_of.assign(s->reqs.size(), -1);
     for (size_t i = 0; i < s->reqs.size(); ++i) {
-        const Request& r = s->reqs[i];
-        if (r.is_decode) continue;
-        if (used >= s->budget) break;
-        int64_t computed = r.num_computed;
+        if (s->reqs[i].is_decode && !skip[i] && p.used < s->budget) {
+            p.picked.emplace_back(i, 1);
+            p.used += 1;
+        }
+    }
+    int32_t longs = 0;
+    for (size_t i = 0; i < s->reqs.size(); ++i) {
+        const Request& q = s->reqs[i];
+        if (q.is_decode || skip[i]) continue;
+        if (p.used >= s->budget) break;
+        const bool is_long = s->cap > 0 && q.num_tokens > s->cap;
+        if (is_long && s->max_long > 0 && longs >= s->max_long) continue;
+        int64_t computed = q.num_computed;
         bool look = false;
-        Hit h;
-        if (s->caching && !r.tokens.empty() && !r.looked_up && r.num_computed == 0) {
-            const int64_t first = s->take_for(r.num_tokens, used);
-            const int64_t lim = first < r.num_tokens - 1 ? first : r.num_tokens - 1;
-            s->lookup(r.tokens, r.scope, (int32_t)(lim > 0 ? lim / s->block_size : 0), h.blocks,
+        StepPlan::Hit h;
+        if (s->caching && !q.tokens.empty() && !q.looked_up && q.num_computed == 0) {
+            const int64_t first = s->take_for(q.num_tokens, p.used);
+            const int64_t lim = first < q.num_tokens - 1 ? first : q.num_tokens - 1;
+            s->lookup(q.tokens, q.scope, (int32_t)(lim > 0 ? lim / s->block_size : 0), h.blocks,
                       h.digests);
             computed = (int64_t)h.blocks.size() * s->block_size;
             look = true;
         }
-        const int64_t take = s->take_for((int64_t)r.num_tokens - computed, used);
+        const int64_t take = s->take_for((int64_t)q.num_tokens - computed, p.used);
         if (take <= 0) continue;
         if (look) {
-            hit_of[i] = (int32_t)hits.size();
-            hits.push_back(std::move(h));
+            p.hit_of[i] = (int32_t)p.hits.size();
+            p.hits.push_back(std::move(h));
         }
-        picked.emplace_back(i, (int32_t)take);
-        used += take;
+        p.picked.emplace_back(i, (int32_t)take);
+        p.used += take;
+        longs += is_long;
     }
-    // capacity of the caller's arrays
-    if ((int64_t)picked.size() > out->max_seqs || used > out->max_tokens) return CPA_ERR_INVALID_ARG;
-    if (!out->req_ids || !out->q_lens || !out->cu_seqlens_q || !out->cached_seq_len ||
-        !out->block_table || !out->slot_mapping)
-        return CPA_ERR_INVALID_ARG;
-    // block growth: all or nothing (prefix hits on reclaimable blocks take
-    // them out of the free count)
-    int64_t need_total = 0;
-    std::vector<int32_t> need_new(picked.size());
+    // block growth (prefix hits on reclaimable blocks take them out of the
+    // free count)
     std::vector<int32_t> claimed;
-    for (size_t k = 0; k < picked.size(); ++k) {
-        const Request& r = s->reqs[picked[k].first];
-        const int32_t hi = hit_of[picked[k].first];
-        const int64_t computed = hi < 0 ? r.num_computed : (int64_t)hits[hi].blocks.size() * s->block_size;
-        const int64_t held = hi < 0 ? (int64_t)r.blocks.size() : (int64_t)hits[hi].blocks.size();
-        const int64_t need = cdiv64(computed + picked[k].second, s->block_size);
-        if (need > s->max_blocks) return CPA_ERR_INVALID_ARG;
-        need_new[k] = (int32_t)(need - held);
-        need_total += need_new[k];
+    p.need_new.resize(p.picked.size());
+    for (size_t k = 0; k < p.picked.size(); ++k) {
+        const Request& q = s->reqs[p.picked[k].first];
+        const int32_t hi = p.hit_of[p.picked[k].first];
+        const int64_t computed = hi < 0 ? q.num_computed : (int64_t)p.hits[hi].blocks.size() * s->block_size;
+        const int64_t held = hi < 0 ? (int64_t)q.blocks.size() : (int64_t)p.hits[hi].blocks.size();
+        const int64_t need = cdiv64(computed + p.picked[k].second, s->block_size);
+        if (need > s->max_blocks) p.too_wide = true;
+        p.need_new[k] = (int32_t)(need - held);
+        p.need_total += p.need_new[k];
         if (hi >= 0)
-            for (int32_t b : hits[hi].blocks)
+            for (int32_t b : p.hits[hi].blocks)
                 if (s->ref[b] == 0) claimed.push_back(b);
     }
     std::sort(claimed.begin(), claimed.end());
     claimed.erase(std::unique(claimed.begin(), claimed.end()), claimed.end());
-    if (need_total > s->num_free() - (int64_t)claimed.size()) return CPA_ERR_OUT_OF_BLOCKS;
+    p.claimed = (int64_t)claimed.size();
+}
+
+}  // namespace
+
+extern "C" {
+
+cpa_status cpa_sched_step(cpa_sched* s, cpa_batch* out) {
+    if (!s || !out) return CPA_ERR_INVALID_ARG;
+    if (!out->req_ids || !out->q_lens || !out->cu_seqlens_q || !out->cached_seq_len ||
+        !out->block_table || !out->slot_mapping)
+        return CPA_ERR_INVALID_ARG;
+    // plan; when the pool cannot hold it, preempt the most recently arrived
+    // request holding blocks (first come, first served: "vLLM Chunked
+    // Prefill ...", section 4) and plan again
+    std::vector<char> skip(s->reqs.size(), 0);
+    s->preempted.clear();
+    StepPlan plan;
+    for (;;) {
+        plan = StepPlan();
+        plan_step(s, skip, plan);
+        if (plan.too_wide) return CPA_ERR_INVALID_ARG;
+        if (plan.need_total <= s->num_free() - plan.claimed) break;
+        if (!s->preemption) return CPA_ERR_OUT_OF_BLOCKS;
+        int64_t victim = -1;
+        for (size_t i = s->reqs.size(); i-- > 0;)
+            if (!skip[i] && !s->reqs[i].blocks.empty()) {
+                victim = (int64_t)i;
+                break;
+            }
+        if (victim < 0) return CPA_ERR_OUT_OF_BLOCKS;
+        s->preempt(s->reqs[(size_t)victim]);
+        skip[(size_t)victim] = 1;
+        s->preempted.push_back(s->reqs[(size_t)victim].id);
+    }
+    auto& picked = plan.picked;
+    const int64_t used = plan.used;
+    // capacity of the caller's arrays
+    if ((int64_t)picked.size() > out->max_seqs || used > out->max_tokens) return CPA_ERR_INVALID_ARG;
     for (size_t k = 0; k < picked.size(); ++k) {
-        const int32_t hi = hit_of[picked[k].first];
+        const int32_t hi = plan.hit_of[picked[k].first];
         if (hi < 0) continue;
         Request& r = s->reqs[picked[k].first];
         r.looked_up = true;
-        for (int32_t b : hits[hi].blocks) s->claim(b);
-        r.blocks = hits[hi].blocks;
+        for (int32_t b : plan.hits[hi].blocks) s->claim(b);
+        r.blocks = plan.hits[hi].blocks;
         r.num_computed = (int32_t)(r.blocks.size() * (size_t)s->block_size);
-        r.digests = hits[hi].digests;
+        r.digests = plan.hits[hi].digests;
     }
     for (size_t k = 0; k < picked.size(); ++k) {
         Request& r = s->reqs[picked[k].first];
-        if (need_new[k] > 0) s->take(need_new[k], r.blocks);
+        if (plan.need_new[k] > 0) s->take(plan.need_new[k], r.blocks);
     }
     // descriptor
     out->cu_seqlens_q[0] = 0;
@@ -515,6 +584,16 @@ cpa_status cpa_sched_slots(const cpa_sched* s, int64_t req_id, int32_t pos0, int
 cpa_status cpa_sched_num_free_blocks(const cpa_sched* s, int32_t* num_free) {
     if (!s || !num_free) return CPA_ERR_INVALID_ARG;
     *num_free = (int32_t)s->num_free();
+    return CPA_OK;
+}
+
+cpa_status cpa_sched_last_preempted(const cpa_sched* s, int64_t* ids, int32_t capacity,
+                                    int32_t* num) {
+    if (!s || !num) return CPA_ERR_INVALID_ARG;
+    if ((int64_t)s->preempted.size() > capacity || (!ids && !s->preempted.empty()))
+        return CPA_ERR_INVALID_ARG;
+    for (size_t i = 0; i < s->preempted.size(); ++i) ids[i] = s->preempted[i];
+    *num = (int32_t)s->preempted.size();
     return CPA_OK;
 }
 

@@ -33,7 +33,8 @@ class HostScheduler:
 
     def __init__(self, num_blocks: int, block_size: int, max_batched_tokens: int,
                  max_blocks_per_seq: int, long_prefill_cap: int = 0, align_to_block: bool = False,
-                 free_order=None, prefix_caching: bool = False):
+                 free_order=None, prefix_caching: bool = False,
+                 max_long_partial_prefills: int = 0, preemption: bool = False):
         self.block_size = block_size
         self.max_blocks = max_blocks_per_seq
         self.budget = max_batched_tokens
@@ -45,6 +46,8 @@ class HostScheduler:
         cfg.long_prefill_cap = long_prefill_cap
         cfg.align_to_block = int(bool(align_to_block))
         cfg.prefix_caching = int(bool(prefix_caching))
+        cfg.max_long_partial_prefills = max_long_partial_prefills
+        cfg.preemption = int(bool(preemption))
         self._order = None
         if free_order is not None:
             self._order = np.ascontiguousarray(free_order, dtype=np.int32)
@@ -110,6 +113,14 @@ class HostScheduler:
                 "cached_seq_len": out["cached_seq_len"][:s],
                 "block_table": out["block_table"][:s], "slot_mapping": out["slot_mapping"][:t],
                 "num_seqs": s, "num_tokens": t}
+
+    def last_preempted(self) -> list:
+        """Ids of the requests the last step preempted."""
+        buf = np.zeros(max(1, self._max_seqs), dtype=np.int64)
+        n = ctypes.c_int32()
+        _lib.check(_lib.lib().cpa_sched_last_preempted(self._h, _i64p(buf), len(buf),
+                                                       ctypes.byref(n)), "cpa_sched_last_preempted")
+        return buf[:n.value].tolist()
 
     def commit(self):
         _lib.check(_lib.lib().cpa_sched_commit(self._h), "cpa_sched_commit")

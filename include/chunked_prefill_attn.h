@@ -247,6 +247,14 @@ typedef struct cpa_sched_config {
                                     0..num_blocks-1), NULL = 0,1,2,...         */
     int32_t prefix_caching;      /* 1: match and register full prompt blocks
                                     of requests given by token ids (below)    */
+    int32_t max_long_partial_prefills; /* prompts longer than long_prefill_cap
+                                    scheduled per step at most (0: no limit);
+                                    later long prompts wait while shorter ones
+                                    behind them run ("vLLM Chunked Prefill
+                                    ...", section 3.3)                         */
+    int32_t preemption;          /* 1: a step whose blocks do not fit preempts
+                                    requests instead of failing (see
+                                    cpa_sched_step)                            */
 } cpa_sched_config;
 
 /* Batch descriptor of one step, written into caller-owned host arrays. */
@@ -306,9 +314,19 @@ cpa_status cpa_sched_add_decode(cpa_sched* sched, int64_t req_id, int32_t contex
 cpa_status cpa_sched_add_partial(cpa_sched* sched, int64_t req_id, int32_t num_prompt_tokens,
                                  int32_t num_computed_tokens);
 
-/* Build the next step (tokens, block growth, descriptor).  On
- * CPA_ERR_OUT_OF_BLOCKS nothing changes (preemption is the caller's). */
+/* Build the next step (tokens, block growth, descriptor).  When the pool
+ * cannot hold the step: without preemption, CPA_ERR_OUT_OF_BLOCKS and
+ * nothing changes; with it ("vLLM Chunked Prefill ...", section 4), the most
+ * recently arrived request holding blocks is preempted (all its blocks
+ * released, its progress reset to position 0, so it recomputes every known
+ * token later) and the step is planned again without it, until it fits;
+ * CPA_ERR_OUT_OF_BLOCKS only when nothing is left to preempt (preemptions
+ * made so far stay made). */
 cpa_status cpa_sched_step(cpa_sched* sched, cpa_batch* batch);
+
+/* Ids of the requests the last cpa_sched_step preempted, in order. */
+cpa_status cpa_sched_last_preempted(const cpa_sched* sched, int64_t* ids, int32_t capacity,
+                                    int32_t* num);
 
 /* Advance every request of the last step; a finished prompt becomes a decode. */
 cpa_status cpa_sched_commit(cpa_sched* sched);

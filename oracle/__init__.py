@@ -25,6 +25,11 @@ block hash chain, full-block matching and the pool's three buckets
 ("Prefill Optimisation ...", sections 3 and 7) and the first-chunk-only
 lookup ("vLLM Chunked Prefill ...", sections 2.2 and 3.1).
 
+``fp8`` has the E4M3 code of a cache element (per-tensor scale) and its
+value, for a cache kept in FP8 ("Prefill Optimisation ...", section 3 names
+the element type as part of a cache entry; the format itself is the
+standard OCP one).
+
 ``rope`` adds rotary position embedding at absolute positions ("Prefill
 Optimisation ...", section 2, "Causal equivalence"; "Chunked Prefill",
 section "From scratch"), in the standard rotary form, which the pages name
@@ -37,4 +42,4 @@ never define it); it is fixed to the consecutive grouping that
 ``torch.nn.functional.scaled_dot_product_attention`` uses and is pinned only
 against that library convention.
 """
-from . import attention, counters, prefix_cache, rope, schedule  # noqa: F401
+from . import attention, counters, fp8, prefix_cache, rope, schedule  # noqa: F401

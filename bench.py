@@ -42,6 +42,7 @@ KERNEL_SOURCES = ("chunked_prefill_paged_amd/csrc/cpa_attn.hip", "chunked_prefil
 TRAFFIC_FILE = "profiles/attn_kernel_10k_prompt_hbm_traffic.txt"
 ROPE_TRAFFIC_FILE = "profiles/prep_kernel_rope_cache_write.txt"
 COPY_PROBE_BYTES = 1 << 30
+FP8_SCALE = 0.05              # per-tensor K and V scale of an fp8 cache (N(0,1) data: no saturation)
 
 
 def _args():
@@ -57,6 +58,9 @@ def _args():
                     help="c2: the 10k prompt (headline line); c5: the 32k prompt, per chunk "
                          "and against one monolithic call; c4: the mixed decode + prefill batch; "
                          "rope: the cache write with rotary embedding fused in, at two chunk shapes")
+    ap.add_argument("--kv-cache", choices=("bf16", "fp8"), default="bf16",
+                    help="KV cache element type for c2/c5/c4: bf16, or E4M3 codes under per-tensor "
+                         "scales (attention still computes in bf16)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device-to-device copy 5 times and exit")
     return ap.parse_args()
@@ -109,7 +113,7 @@ class PromptBench:
     """One chunked prompt (the 10k prompt by default), its device buffers and
     the per-chunk calls."""
 
-    def __init__(self, kv_segment_size, split_pre, workload="c2"):
+    def __init__(self, kv_segment_size, split_pre, workload="c2", kv_fp8=False):
         import torch
         from chunked_prefill_paged_amd import AttnCall, HostScheduler, cache_shapes
         from synth import free_block_order, get_workload, prompt_qkv
@@ -124,8 +128,9 @@ class PromptBench:
         self.v = torch.from_numpy(v32).to(torch.bfloat16).to(dev)
         self.out = torch.empty_like(self.q)
         ks, vs = cache_shapes(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
-        self.k_cache = torch.zeros(ks, dtype=torch.bfloat16, device=dev)
-        self.v_cache = torch.zeros(vs, dtype=torch.bfloat16, device=dev)
+        cache_t = torch.uint8 if kv_fp8 else torch.bfloat16
+        self.k_cache = torch.zeros(ks, dtype=cache_t, device=dev)
+        self.v_cache = torch.zeros(vs, dtype=cache_t, device=dev)
         self.max_blocks = -(-w.prompt_len // w.block_size)
         self.sched = HostScheduler(w.num_blocks, w.block_size, w.max_batched_tokens,
                                    self.max_blocks, free_order=free_block_order(w.num_blocks, w.seed))
@@ -153,7 +158,8 @@ class PromptBench:
                             block_table=d_i32[3:].view(1, self.max_blocks), slot_mapping=None,
                             h_cu_seqlens_q=np.array([0, n], np.int32),
                             h_cached_seq_len=np.array([pos], np.int32),
-                            kv_segment_size=kv_segment_size, split_keys_prefill=split_pre)
+                            kv_segment_size=kv_segment_size, split_keys_prefill=split_pre,
+                            k_scale=FP8_SCALE, v_scale=FP8_SCALE)
             ws_bytes = max(ws_bytes, call.workspace_bytes())
             self.calls.append(call)
             self.dev_desc.append(d_i32)
@@ -266,7 +272,7 @@ def run_long_prompt(args):
     prompt against one monolithic causal call over all 32k tokens."""
     import torch
     S = 4096 if args.kv_segment_size == 1024 else args.kv_segment_size
-    bench = PromptBench(S, args.split_keys_prefill, workload="c5")
+    bench = PromptBench(S, args.split_keys_prefill, workload="c5", kv_fp8=args.kv_cache == "fp8")
     w = bench.w
     steps = max(1, min(args.steps, 5))
     warm = max(1, min(args.warmup, 2))
@@ -302,7 +308,7 @@ def run_long_prompt(args):
                     v_cache=bench.v_cache, out=bench.out, cu_seqlens_q=cu, cached_seq_len=cached,
                     block_table=bt, slot_mapping=slots, h_cu_seqlens_q=np.array([0, P], np.int32),
                     h_cached_seq_len=np.array([0], np.int32), kv_segment_size=S,
-                    split_keys_prefill=args.split_keys_prefill)
+                    split_keys_prefill=args.split_keys_prefill, k_scale=FP8_SCALE, v_scale=FP8_SCALE)
     ws = torch.empty(mono.workspace_bytes(), dtype=torch.uint8, device=dev)
     mono.set_workspace(ws)
     mono_s = _time_steps(torch, mono, steps, warm)
@@ -313,7 +319,8 @@ def run_long_prompt(args):
         "steps": steps, "warmup": warm, "ms_per_step": round(chunked_s * 1e3, 3),
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "32,768-token prompt in 16 chunks of 2048 (cached 0..30720), "
-                               f"H64/G8/D128, block_size 16, kv_segment_size {S}"},
+                               f"H64/G8/D128, block_size 16, kv_segment_size {S}",
+                   "kv_cache": args.kv_cache},
         "gflop_per_step": round(flops / 1e9, 2),
         "attention_ms_per_chunk": [round(x, 4) for x in per_chunk_ms],
         "attention_tflops_per_chunk": per_chunk_tf,
@@ -352,13 +359,18 @@ def run_mixed_batch(args):
     T = int(b["num_tokens"])
     dev = "cuda"
     ks, vs = cache_shapes(nb, G, bs, D)
-    k_cache = torch.empty(ks, dtype=torch.bfloat16, device=dev)
-    v_cache = torch.empty(vs, dtype=torch.bfloat16, device=dev)
+    fp8 = args.kv_cache == "fp8"
+    k_cache = torch.empty(ks, dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    v_cache = torch.empty(vs, dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed)
     for t in (k_cache, v_cache):             # the cached context: seeded N(0,1)
         for i in range(0, nb, 8192):
-            t[i:i + 8192].normal_(generator=gen)
+            if fp8:                          # its E4M3 codes under FP8_SCALE
+                blk = torch.randn(t[i:i + 8192].shape, generator=gen, device=dev) / FP8_SCALE
+                t[i:i + 8192] = blk.to(torch.float8_e4m3fn).view(torch.uint8)
+            else:
+                t[i:i + 8192].normal_(generator=gen)
     q = torch.randn((T, H, D), generator=gen, device=dev).to(torch.bfloat16)
     kn = torch.randn((T, G, D), generator=gen, device=dev).to(torch.bfloat16)
     vn = torch.randn((T, G, D), generator=gen, device=dev).to(torch.bfloat16)
@@ -379,7 +391,8 @@ def run_mixed_batch(args):
                         cached_seq_len=cached[lo:hi].contiguous(),
                         block_table=table[lo:hi].contiguous(), slot_mapping=slots[t0:t1].contiguous(),
                         h_cu_seqlens_q=cu_h[lo:hi + 1] - t0, h_cached_seq_len=cached_h[lo:hi],
-                        kv_segment_size=S, split_keys_prefill=args.split_keys_prefill)
+                        kv_segment_size=S, split_keys_prefill=args.split_keys_prefill,
+                        k_scale=FP8_SCALE, v_scale=FP8_SCALE)
         call.set_workspace(torch.empty(call.workspace_bytes(), dtype=torch.uint8, device=dev))
         return call
 
@@ -389,7 +402,8 @@ def run_mixed_batch(args):
     t_mixed = _time_steps(torch, mixed, steps, warm)
     t_dec = _time_steps(torch, decodes, steps, warm)
     t_pre = _time_steps(torch, prefill, steps, warm)
-    dec_bytes = sum(2 * (L + 1) * G * D * 2 for L in ctx)          # K and V each decode reads
+    eb = 1 if fp8 else 2
+    dec_bytes = sum(2 * (L + 1) * G * D * eb for L in ctx)         # K and V each decode reads
     n_pre = T - 256
     pre_flops = 4 * H * D * (n_pre * pf_cached + n_pre * (n_pre + 1) // 2)
     dec_flops = sum(4 * H * D * (L + 1) for L in ctx)
@@ -400,7 +414,8 @@ def run_mixed_batch(args):
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"256 decodes (context 16*U{{64..2048}}) + 1792-token chunk at "
                                f"cached 30720, budget 2048, bs16, S{S}, H32/G8/D128, "
-                               f"pool {nb} blocks ({2 * nb * G * bs * D * 2 / 1e9:.1f} GB K+V)"},
+                               f"pool {nb} blocks ({2 * nb * G * bs * D * eb / 1e9:.1f} GB K+V)",
+                   "kv_cache": args.kv_cache},
         "mixed_ms": round(t_mixed * 1e3, 4),
         "decode_only_ms": round(t_dec * 1e3, 4),
         "decode_kv_gb": round(dec_bytes / 1e9, 3),
@@ -507,7 +522,7 @@ def main():
     if args.workload == "rope":
         run_rope(args)
         return
-    bench = PromptBench(args.kv_segment_size, args.split_keys_prefill)
+    bench = PromptBench(args.kv_segment_size, args.split_keys_prefill, kv_fp8=args.kv_cache == "fp8")
     flops = bench.flops_per_step()
     for _ in range(args.warmup):
         bench.step()
@@ -544,17 +559,18 @@ def main():
             "workload": "10k-token GQA chunked prefill: chunks 2048x4+1808 (cached 0..8192), "
                         f"H32/G8/D128, block_size 128, kv_segment_size {args.kv_segment_size}",
             "global_batch": 1, "seq_len": w.prompt_len, "parallelism": "none (1 GPU)",
+            "kv_cache": args.kv_cache,
         },
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "gflop_per_step": round(flops / 1e9, 2),
         "attention_ms_per_chunk": [round(x, 4) for x in per_chunk_ms],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": recorded_traffic(),
+                     "traffic": recorded_traffic() if args.kv_cache == "bf16" else None,
                      "kernel": "attn_kernel<bf16,128> (+ merge_kernel when rows are split)"},
         "plan": [{"items": p["num_items"], "merge_rows": p["num_merge_rows"]} for p in bench.plan],
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.kv_cache == "bf16":
         line["cpu_baseline"] = cpu_baseline(bench.w, bench.max_blocks)
     print(json.dumps(line), flush=True)
 

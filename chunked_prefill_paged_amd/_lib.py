@@ -23,6 +23,7 @@ CPA_ERR_NOT_FOUND = 7
 
 CPA_BF16 = 0
 CPA_FP32 = 1
+CPA_FP8_E4M3 = 2
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -42,6 +43,7 @@ class AttnArgs(ctypes.Structure):
         ("cu_seqlens_q", _vp), ("cached_seq_len", _vp), ("block_table", _vp),
         ("slot_mapping", _vp), ("out", _vp), ("lse", _vp), ("workspace", _vp),
         ("workspace_bytes", ctypes.c_size_t), ("h_cu_seqlens_q", _vp), ("h_cached_seq_len", _vp),
+        ("kv_dtype", _i32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
     ]
 
 

@@ -16,11 +16,18 @@ from . import _lib
 _DTYPES = {"bfloat16": _lib.CPA_BF16, "float32": _lib.CPA_FP32}
 
 
+_FP8_CACHE = ("uint8", "float8_e4m3fn")     # one-byte E4M3 codes
+
+
 def _dtype_code(t) -> int:
     name = str(t.dtype).replace("torch.", "")
     if name not in _DTYPES:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return _DTYPES[name]
+
+
+def _is_fp8_cache(t) -> bool:
+    return str(t.dtype).replace("torch.", "") in _FP8_CACHE
 
 
 def _ptr(t) -> int:
@@ -51,7 +58,11 @@ class AttnCall:
     def __init__(self, *, q, k_new, v_new, k_cache, v_cache, out, cu_seqlens_q,
                  cached_seq_len, block_table, slot_mapping, h_cu_seqlens_q,
                  h_cached_seq_len, kv_segment_size, scale=None, lse=None, workspace=None,
-                 decode_token_threshold=0, split_keys_prefill=0, split_keys_decode=0):
+                 decode_token_threshold=0, split_keys_prefill=0, split_keys_decode=0,
+                 k_scale=1.0, v_scale=1.0):
+        """A cache of one-byte elements (uint8 or float8_e4m3fn) holds E4M3
+        codes under per-tensor scales ``k_scale`` / ``v_scale``; the other
+        tensors are then bfloat16."""
         num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
         if tuple(v_cache.shape) != (num_blocks, num_kv_heads, head_dim, block_size):
             raise ValueError(f"v_cache must be {(num_blocks, num_kv_heads, head_dim, block_size)}")
@@ -67,7 +78,12 @@ class AttnCall:
         if slot_mapping is not None and str(slot_mapping.dtype) != "torch.int64":
             raise TypeError("slot_mapping must be int64")
         a = _lib.AttnArgs()
-        a.dtype = _dtype_code(k_cache)
+        if _is_fp8_cache(k_cache):
+            a.dtype = _dtype_code(k_new)
+            a.kv_dtype = _lib.CPA_FP8_E4M3
+            a.k_scale, a.v_scale = float(k_scale), float(v_scale)
+        else:
+            a.dtype = _dtype_code(k_cache)
         a.num_seqs = len(h_cu) - 1
         a.total_q = total_q
         a.num_heads = num_heads

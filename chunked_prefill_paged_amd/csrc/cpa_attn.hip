@@ -162,10 +162,16 @@ struct AttnParams {
     int32_t dec_thresh;
     int32_t split_pre;
     int32_t split_dec;
-    float scale_log2;   // softmax scale * log2(e)
+    float scale_log2;   // softmax scale * log2(e) (* the K scale of an fp8 cache)
+    float v_scale;      // V scale of an fp8 cache (1 otherwise)
 };
 
-template <typename T, int D>
+// FP8: the cache holds E4M3 codes (K [nb, G, bs, D], V^T [nb, G, D, bs], one
+// byte each); tiles are gathered through registers one tile ahead, turned
+// into bf16 exactly (every E4M3 value is a bf16 value) and stored into the
+// same LDS tiles as a bf16 cache, so the products do not change.  The K
+// scale is folded into the softmax scale and the V scale into the output.
+template <typename T, int D, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     using E = Elem<T>;
     using Frag = typename E::Frag;
@@ -347,6 +353,88 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                 const char* base = vc_g + (size_t)blk * blk_bytes;
                 const uint32_t off = (uint32_t)(((v_d0 + i * RV) * bs + ((ts + kk) & (bs - 1))) * (int)sizeof(T));
                 gather16(base + off, lds0 + sl * 1024);
+            }
+        }
+    };
+    // FP8 gathers: per thread NL8 16-byte chunks of K (16 consecutive d of one
+    // key) and of V^T (16 consecutive keys of one d), zero past the sequence
+    constexpr int NC8K = D / 16;                    // fp8 chunks per K row
+    constexpr int NC8V = kKeys / 16;                // fp8 chunks per V^T row
+    constexpr int NL8 = kKeys * NC8K / kThreads;
+    static_assert(!FP8 || (NL8 * kThreads == kKeys * NC8K && NL8 * kThreads == D * NC8V),
+                  "fp8 tile must split evenly over threads");
+    u32x4 f8k[FP8 ? NL8 : 1], f8v[FP8 ? NL8 : 1];
+    auto load_tile_fp8 = [&](int ts, int btv) {
+        if constexpr (FP8) {
+            const uint8_t* k8 = (const uint8_t*)p.k_cache;
+            const uint8_t* v8 = (const uint8_t*)p.v_cache;
+#pragma unroll
+            for (int i = 0; i < NL8; ++i) {
+                const int cidx = i * kThreads + tid;
+                const int key = cidx / NC8K, c8 = cidx % NC8K;
+                const int j = ts + key;
+                const uint32_t bi = bs >= kKeys ? (uint32_t)__builtin_amdgcn_readlane(btv, 0)
+                                                : (uint32_t)__shfl(btv, key >> lbs);
+                const uint32_t blk = min(bi, nb_max);
+                u32x4 val = {0u, 0u, 0u, 0u};
+                if (j < kv_len)
+                    val = *(const u32x4*)(k8 + (((size_t)blk * G + g) * bs + (j & (bs - 1))) * D + c8 * 16);
+                f8k[i] = val;
+            }
+#pragma unroll
+            for (int i = 0; i < NL8; ++i) {
+                const int cidx = i * kThreads + tid;
+                const int d = cidx / NC8V, kc = cidx % NC8V;
+                const int j = ts + kc * 16;              // 16 keys of one block (bs >= 16)
+                const uint32_t bi = bs >= kKeys ? (uint32_t)__builtin_amdgcn_readlane(btv, 0)
+                                                : (uint32_t)__shfl(btv, (kc * 16) >> lbs);
+                const uint32_t blk = min(bi, nb_max);
+                u32x4 val = {0u, 0u, 0u, 0u};
+                if (j < kv_len) {
+                    val = *(const u32x4*)(v8 + (((size_t)blk * G + g) * D + d) * bs + (j & (bs - 1)));
+                    if (kv_len - j < 16) {
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            const int keep = min(max(kv_len - j - 4 * w, 0), 4);
+                            val[w] &= keep >= 4 ? 0xffffffffu : ((1u << (8 * keep)) - 1u);
+                        }
+                    }
+                }
+                f8v[i] = val;
+            }
+        }
+    };
+    // 16 E4M3 codes -> 16 bf16 (two 16-byte chunks)
+    auto fp8_to_bf16 = [&](u32x4 x, u32x4& lo, u32x4& hi) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, false));
+            const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, true));
+            if (w < 2) { lo[2 * w] = a; lo[2 * w + 1] = c; }
+            else { hi[2 * w - 4] = a; hi[2 * w - 3] = c; }
+        }
+    };
+    auto store_tile_fp8 = [&](int buf) {
+        if constexpr (FP8) {
+#pragma unroll
+            for (int i = 0; i < NL8; ++i) {
+                const int cidx = i * kThreads + tid;
+                const int key = cidx / NC8K, c8 = cidx % NC8K;
+                const int sw = swap_bits23(key & 31) & SWK;
+                u32x4 lo, hi;
+                fp8_to_bf16(f8k[i], lo, hi);
+                *(u32x4*)&lds_k[buf][key * D + ((2 * c8) ^ sw) * EPC] = lo;
+                *(u32x4*)&lds_k[buf][key * D + ((2 * c8 + 1) ^ sw) * EPC] = hi;
+            }
+#pragma unroll
+            for (int i = 0; i < NL8; ++i) {
+                const int cidx = i * kThreads + tid;
+                const int d = cidx / NC8V, kc = cidx % NC8V;
+                const int sw = ((d & 7) ^ ((d >> 3) & 1)) & SWV;
+                u32x4 lo, hi;
+                fp8_to_bf16(f8v[i], lo, hi);
+                *(u32x4*)&lds_v[buf][d * kKeys + ((2 * kc) ^ sw) * EPC] = lo;
+                *(u32x4*)&lds_v[buf][d * kKeys + ((2 * kc + 1) ^ sw) * EPC] = hi;
             }
         }
     };
@@ -631,17 +719,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
         Frag pf[NKS];
         auto tstart = [&](int u) { return (tile0 + u) * kKeys; };
         int btn = 0;                     // block ids of tile u + 1
-        if (nfull > 0) {
-            const int bt0 = load_bt(tstart(0));
-            dma_k(tstart(0), 0, bt0);
-            dma_v(tstart(0), 0, bt0);
+        // (an fp8 cache reads the table for every tile, the last included:
+        // columns stay within the sequence's blocks)
+        const int last_col = (kv_len - 1) >> lbs;
+        auto load_bt8 = [&](int ts) -> int {
+            return bt[min((ts >> lbs) + min(lane, nbt - 1), last_col)];
+        };
+        if constexpr (FP8) {
+            load_tile_fp8(tstart(0), load_bt8(tstart(0)));
+            store_tile_fp8(0);
+            if (ntiles > 1) btn = load_bt8(tstart(1));
+        } else {
+            if (nfull > 0) {
+                const int bt0 = load_bt(tstart(0));
+                dma_k(tstart(0), 0, bt0);
+                dma_v(tstart(0), 0, bt0);
+            }
+            if (nfull > 1) btn = load_bt(tstart(1));
         }
-        if (nfull > 1) btn = load_bt(tstart(1));
         wait_vmem();                     // Q and the first block ids
         for (int u = 0; u < ntiles; ++u) {
             const int ts = tstart(u);
             const int buf = u & 1;
-            if (u >= nfull) {            // the sequence's last tile
+            if (!FP8 && u >= nfull) {    // the sequence's last tile
                 load_tile_edge(ts);
                 store_tile(buf);
             }
@@ -649,20 +749,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             // the barrier for everyone's); all waves are done with buf ^ 1
             wait_vmem();
             __syncthreads();
-            if (u + 1 < nfull) {
-                dma_k(tstart(u + 1), buf ^ 1, btn);
-                dma_v(tstart(u + 1), buf ^ 1, btn);
-            }
-            if (u + 2 < nfull) btn = load_bt(tstart(u + 2));
-            if (!active(ts)) continue;
-            const bool masked = (ts + kKeys - 1 > c + wt_min) || (ts + kKeys > k1);
-            if constexpr (kHandOrdered) {
-                compute_tile(buf, ts, masked);
+            if constexpr (FP8) {
+                if (u + 1 < ntiles) load_tile_fp8(tstart(u + 1), btn);
+                if (u + 2 < ntiles) btn = load_bt8(tstart(u + 2));
             } else {
-                qk(buf, S);
-                update_ref(mask_max(ts, S));
-                probs(S, pf);
-                pv(buf, pf);
+                if (u + 1 < nfull) {
+                    dma_k(tstart(u + 1), buf ^ 1, btn);
+                    dma_v(tstart(u + 1), buf ^ 1, btn);
+                }
+                if (u + 2 < nfull) btn = load_bt(tstart(u + 2));
+            }
+            if (active(ts)) {
+                const bool masked = (ts + kKeys - 1 > c + wt_min) || (ts + kKeys > k1);
+                if constexpr (kHandOrdered) {
+                    compute_tile(buf, ts, masked);
+                } else {
+                    qk(buf, S);
+                    update_ref(mask_max(ts, S));
+                    probs(S, pf);
+                    pv(buf, pf);
+                }
+            }
+            // the next tile of an fp8 cache goes into the other buffer, which
+            // every wave finished reading before this tile's barrier
+            if constexpr (FP8) {
+                if (u + 1 < ntiles) store_tile_fp8(buf ^ 1);
             }
         }
     }
@@ -670,7 +781,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (!row_ok) return;
     if (nsplit == 1) {
-        const float inv = 1.f / l_tot;
+        const float inv = p.v_scale / l_tot;
         T* op = (T*)p.out + ((size_t)(q0 + t) * p.num_heads + head) * D;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -703,7 +814,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                 const int d = dt * 32 + rq * 8 + half * 4;
                 f32x4 v;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = oacc[dt][rq * 4 + i];
+                for (int i = 0; i < 4; ++i) v[i] = oacc[dt][rq * 4 + i] * p.v_scale;
                 *(f32x4*)(po + d) = v;
             }
         }
@@ -797,6 +908,8 @@ struct PrepParams {
     int32_t rope;
     int32_t rope_wgs;
     float rope_theta;
+    // fp8 cache: codes of x * inv_k (K) and x * inv_v (V)
+    float inv_k, inv_v;
     const void* q;
     void* q_out;
     // plan (only when plan != 0)
@@ -908,7 +1021,15 @@ __device__ void rope_freqs(const PrepParams& p, double* s_freq) {
     if (threadIdx.x < D / 2) s_freq[threadIdx.x] = pow((double)p.rope_theta, -2.0 * threadIdx.x / D);
 }
 
-template <typename T, int D, bool ROPE>
+// E4M3 codes of scaled values: clamped to the largest finite magnitude (448),
+// then rounded to nearest, ties to even, by the conversion instruction.
+__device__ inline float sat448(float x) { return fminf(fmaxf(x, -448.f), 448.f); }
+__device__ inline uint32_t fp8_pack4(float a, float b, float c, float d) {
+    const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), (int)w, true);
+}
+
+template <typename T, int D, bool ROPE, bool FP8>
 __device__ void cache_write(const PrepParams& p, char* smem) {
     constexpr int EPC = 16 / sizeof(T);
     constexpr int NCK = D / EPC;
@@ -974,7 +1095,23 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
         dst[1] = vv.y;
         dst[2] = vv.z;
         dst[3] = vv.w;
-        if constexpr (!ROPE) {
+        if constexpr (FP8) {
+            // 8 bf16 of K -> 8 codes at the slot's row (D bytes)
+            const u32x4 kv = *(const u32x4*)(kn + src);
+            const int64_t slot = s_slot[tk];
+            if (slot >= 0 && slot < nslots) {
+                const int64_t blk = slot >> p.log2_bs;
+                const int off = (int)(slot & (bs - 1));
+                T e[8];
+                __builtin_memcpy(e, &kv, 16);
+                uint2 q8;
+                q8.x = fp8_pack4((float)e[0] * p.inv_k, (float)e[1] * p.inv_k, (float)e[2] * p.inv_k,
+                                 (float)e[3] * p.inv_k);
+                q8.y = fp8_pack4((float)e[4] * p.inv_k, (float)e[5] * p.inv_k, (float)e[6] * p.inv_k,
+                                 (float)e[7] * p.inv_k);
+                *(uint2*)((uint8_t*)p.k_cache + ((blk * G + g) * bs + off) * D + ch * 8) = q8;
+            }
+        } else if constexpr (!ROPE) {
             const u32x4 kv = *(const u32x4*)(kn + src);
             const int64_t slot = s_slot[tk];
             if (slot >= 0 && slot < nslots) {
@@ -994,9 +1131,16 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
         if (slot >= 0 && slot < nslots) {
             const int64_t blk = slot >> p.log2_bs;
             const int off = (int)(slot & (bs - 1));
-            T* col = vc + (blk * G + g) * D * (int64_t)bs + off;
-            for (int d = wave * kLanesD + lane / kCacheTok; d < D; d += 4 * kLanesD)
-                col[(size_t)d * bs] = tile[tk * LD + d];
+            if constexpr (FP8) {
+                uint8_t* col = (uint8_t*)p.v_cache + (blk * G + g) * D * (int64_t)bs + off;
+                for (int d = wave * kLanesD + lane / kCacheTok; d < D; d += 4 * kLanesD)
+                    col[(size_t)d * bs] = (uint8_t)__builtin_amdgcn_cvt_pk_fp8_f32(
+                        sat448((float)tile[tk * LD + d] * p.inv_v), 0.f, 0, false);
+            } else {
+                T* col = vc + (blk * G + g) * D * (int64_t)bs + off;
+                for (int d = wave * kLanesD + lane / kCacheTok; d < D; d += 4 * kLanesD)
+                    col[(size_t)d * bs] = tile[tk * LD + d];
+            }
         }
     }
 }
@@ -1154,12 +1298,12 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
 
 // Grid: cache_wgs cache-write workgroups, then (with ROPE) rope_wgs
 // query-rotation workgroups, then (with a plan) one plan builder.
-template <typename T, int D, bool ROPE>
+template <typename T, int D, bool ROPE, bool FP8>
 __global__ __launch_bounds__(kThreads) void prep_kernel(const PrepParams p) {
     __shared__ __attribute__((aligned(16))) char smem[kPrepSmem];
     const int wg = blockIdx.x;
     if (wg < p.cache_wgs) {
-        cache_write<T, D, ROPE>(p, smem);
+        cache_write<T, D, ROPE, FP8>(p, smem);
         return;
     }
     if constexpr (ROPE) {
@@ -1195,6 +1339,14 @@ cpa_status check_common(const cpa_attn_args* a) {
     if (a->head_dim <= 0 || a->block_size <= 0 || a->num_blocks <= 0) return CPA_ERR_INVALID_ARG;
     if (a->head_dim != 64 && a->head_dim != 128) return CPA_ERR_UNSUPPORTED;
     if (!is_pow2(a->block_size) || a->block_size < 8 || a->block_size > 512) return CPA_ERR_UNSUPPORTED;
+    // cache element type: that of dtype, or E4M3 codes under bf16 q/k/v/out
+    if (a->kv_dtype != 0 && a->kv_dtype != a->dtype && a->kv_dtype != CPA_FP8_E4M3)
+        return CPA_ERR_INVALID_ARG;
+    if (a->kv_dtype == CPA_FP8_E4M3) {
+        if (a->dtype != CPA_BF16 || a->block_size < 16) return CPA_ERR_UNSUPPORTED;
+        for (float sc : {a->k_scale, a->v_scale})
+            if (!std::isfinite(sc) || sc < 0.f) return CPA_ERR_INVALID_ARG;
+    }
     if ((int64_t)a->num_blocks * a->block_size > (int64_t)1 << 40) return CPA_ERR_INVALID_ARG;
     return CPA_OK;
 }
@@ -1265,10 +1417,17 @@ cpa_status check_pointers(const cpa_attn_args* a, bool attention) {
     return CPA_OK;
 }
 
-template <typename T, int D>
+inline bool kv_fp8(const cpa_attn_args* a) { return a->kv_dtype == CPA_FP8_E4M3; }
+inline float scale_or_one(float s) { return s == 0.f ? 1.f : s; }
+
+template <typename T, int D, bool FP8>
 cpa_status launch_prep(const cpa_attn_args* a, const Resolved* r, bool plan, const cpa_rope_args* rope,
                        hipStream_t stream) {
     PrepParams p{};
+    if constexpr (FP8) {
+        p.inv_k = 1.f / scale_or_one(a->k_scale);
+        p.inv_v = 1.f / scale_or_one(a->v_scale);
+    }
     p.k_new = a->k_new;
     p.v_new = a->v_new;
     p.k_cache = a->k_cache;
@@ -1311,14 +1470,19 @@ cpa_status launch_prep(const cpa_attn_args* a, const Resolved* r, bool plan, con
     }
     const int grid = p.cache_wgs + p.rope_wgs + (plan ? 1 : 0);
     if (grid == 0) return CPA_OK;
-    if (rope)
-        hipLaunchKernelGGL((prep_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((prep_kernel<T, D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    if constexpr (FP8) {
+        if (rope) return CPA_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL((prep_kernel<T, D, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    } else {
+        if (rope)
+            hipLaunchKernelGGL((prep_kernel<T, D, true, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((prep_kernel<T, D, false, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    }
     return hipGetLastError() == hipSuccess ? CPA_OK : CPA_ERR_HIP;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FP8>
 cpa_status launch_attention(const cpa_attn_args* a, const Resolved* r, hipStream_t stream) {
     char* ws = (char*)a->workspace;
     if (r->items > 0) {
@@ -1347,9 +1511,10 @@ cpa_status launch_attention(const cpa_attn_args* a, const Resolved* r, hipStream
         p.dec_thresh = r->dec_thresh;
         p.split_pre = r->split_pre;
         p.split_dec = r->split_dec;
-        p.scale_log2 = a->scale * 1.44269504088896340736f;
+        p.scale_log2 = a->scale * 1.44269504088896340736f * (FP8 ? scale_or_one(a->k_scale) : 1.f);
+        p.v_scale = FP8 ? scale_or_one(a->v_scale) : 1.f;
         const int grid = (int)(r->items * a->num_kv_heads);
-        hipLaunchKernelGGL((attn_kernel<T, D>), dim3(grid), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((attn_kernel<T, D, FP8>), dim3(grid), dim3(kThreads), 0, stream, p);
         if (hipGetLastError() != hipSuccess) return CPA_ERR_HIP;
     }
     if (r->merge > 0) {
@@ -1380,11 +1545,14 @@ namespace {
 
 cpa_status prep_dispatch(const cpa_attn_args* a, const Resolved* r, bool plan, const cpa_rope_args* rope,
                          hipStream_t s) {
+    if (kv_fp8(a))
+        return a->head_dim == 128 ? launch_prep<__bf16, 128, true>(a, r, plan, rope, s)
+                                  : launch_prep<__bf16, 64, true>(a, r, plan, rope, s);
     if (a->dtype == CPA_BF16)
-        return a->head_dim == 128 ? launch_prep<__bf16, 128>(a, r, plan, rope, s)
-                                  : launch_prep<__bf16, 64>(a, r, plan, rope, s);
-    return a->head_dim == 128 ? launch_prep<float, 128>(a, r, plan, rope, s)
-                              : launch_prep<float, 64>(a, r, plan, rope, s);
+        return a->head_dim == 128 ? launch_prep<__bf16, 128, false>(a, r, plan, rope, s)
+                                  : launch_prep<__bf16, 64, false>(a, r, plan, rope, s);
+    return a->head_dim == 128 ? launch_prep<float, 128, false>(a, r, plan, rope, s)
+                              : launch_prep<float, 64, false>(a, r, plan, rope, s);
 }
 
 // Host-visible checks of a rotary-embedding request: positions come from
@@ -1401,11 +1569,14 @@ cpa_status check_rope(const cpa_attn_args* a, const cpa_rope_args* rope) {
 }
 
 cpa_status attn_dispatch(const cpa_attn_args* a, const Resolved* r, hipStream_t s) {
+    if (kv_fp8(a))
+        return a->head_dim == 128 ? launch_attention<__bf16, 128, true>(a, r, s)
+                                  : launch_attention<__bf16, 64, true>(a, r, s);
     if (a->dtype == CPA_BF16)
-        return a->head_dim == 128 ? launch_attention<__bf16, 128>(a, r, s)
-                                  : launch_attention<__bf16, 64>(a, r, s);
+        return a->head_dim == 128 ? launch_attention<__bf16, 128, false>(a, r, s)
+                                  : launch_attention<__bf16, 64, false>(a, r, s);
     if (a->head_dim == 128) return CPA_ERR_UNSUPPORTED;   // fp32 D=128 needs 128 KiB of LDS tiles
-    return launch_attention<float, 64>(a, r, s);
+    return launch_attention<float, 64, false>(a, r, s);
 }
 
 cpa_status check_workspace(const cpa_attn_args* a, const Resolved* r) {

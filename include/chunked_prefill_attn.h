@@ -74,7 +74,8 @@ typedef enum cpa_status {
 
 typedef enum cpa_dtype {
     CPA_BF16 = 0,                 /* bfloat16 in/out, float32 accumulation     */
-    CPA_FP32 = 1                  /* float32 throughout                        */
+    CPA_FP32 = 1,                 /* float32 throughout                        */
+    CPA_FP8_E4M3 = 2              /* KV cache only (kv_dtype): OCP E4M3 codes  */
 } cpa_dtype;
 
 /* Per-call attention metadata: the pages' metadata dict ("Prefill
@@ -118,6 +119,16 @@ typedef struct cpa_attn_args {
     size_t workspace_bytes;
     const int32_t* h_cu_seqlens_q;  /* host copy of cu_seqlens_q (grid sizing)  */
     const int32_t* h_cached_seq_len;/* host copy of cached_seq_len             */
+    /* Cache element type ("Prefill Optimisation ...", section 3 counts the
+     * element type among what makes a cache entry): 0 (or dtype) keeps
+     * dtype; CPA_FP8_E4M3 stores one-byte OCP E4M3 codes, with dtype
+     * CPA_BF16 and block_size >= 16 (else CPA_ERR_UNSUPPORTED).  A stored
+     * code is that of x * (1/scale), the product in float, clamped to
+     * +-448, rounded to nearest even; its value is code * scale.  k_cache
+     * and v_cache keep their layouts with one byte per element. */
+    int32_t kv_dtype;
+    float   k_scale;                /* fp8 cache: K scale, > 0 (0 means 1)     */
+    float   v_scale;                /* fp8 cache: V scale, > 0 (0 means 1)     */
 } cpa_attn_args;
 
 /* Work decomposition the library derives from the host mirrors. */

@@ -249,6 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     }
 
     float m_run = -INFINITY;
+    float m2 = -INFINITY;        // the hand-ordered path's reference, in log2 units
     float l_run = 0.f;
     f32x16 oacc[NDT];
 #pragma unroll
@@ -600,18 +601,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             };
             // fragment j of the tile's 32 LDS reads: K fragments 0..15, then V 0..15
             auto frag = [&](int j) { return j < 16 ? kfrag(j) : vfrag(j - 16); };
-            auto decide = [&](float hm) {
-                if (__builtin_amdgcn_ballot_w64((hm - m_run) * sl2e > 8.f)) {
-                    const float pm = fmaxf(hm, __shfl_xor(hm, 32));
-                    const bool g = (pm - m_run) * sl2e > 8.f;
-                    const float m_new = g ? pm : m_run;
-                    const float alpha = g ? __builtin_amdgcn_exp2f((m_run - m_new) * sl2e) : 1.f;
-                    l_run *= alpha;
-#pragma unroll
-                    for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
-                    m_run = m_new;
-                }
-            };
             f32x16 S0 = {}, S1 = {};
             bf16x8 fr[4];
             u32x4 pw[4];
@@ -625,13 +614,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                     if (j > lim || j >= k1) S[r] = -INFINITY;
                 }
             };
-            // exp/sum/convert of two scores of S (registers r, r+1) into pw
-            auto ex2 = [&](const f32x16& S, int ks, int r, float nm) {
-                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2e, nm));
-                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r + 1], sl2e, nm));
+            // Scores become exp2 arguments t = S * scale * log2(e) - m2 in
+            // place (m2: the row's reference maximum in log2 units, taken as
+            // 0 while unset).  The block maximum is taken on t: fma results
+            // need no NaN quieting, so one v_max3 folds two scores.
+            auto ref_nm = [&]() { return (m2 == -INFINITY) ? 0.f : -m2; };
+            // one v_max3 per score pair, chained (the compiler otherwise
+            // builds a tree of two-input maxima)
+            auto max3 = [](float a, float b, float c) {
+                float d;
+                asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+                return d;
+            };
+            auto tx = [&](f32x16& S, int r, float nm) {
+                S[r] = __builtin_fmaf(S[r], sl2e, nm);
+                S[r + 1] = __builtin_fmaf(S[r + 1], sl2e, nm);
+            };
+            // exp/sum/convert of registers r, r+1 of t into pw (the empty
+            // asm consumes the results where they are computed: a
+            // speculative exp that a rescale recomputes would otherwise be
+            // sunk by the compiler past the decision, out of its MFMA phase)
+            auto ex2 = [&](const f32x16& S, int ks, int r) {
+                const float e0 = __builtin_amdgcn_exp2f(S[r]);
+                const float e1 = __builtin_amdgcn_exp2f(S[r + 1]);
                 rs += e0 + e1;
                 const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
-                pw[ks][(r & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
+                const uint32_t w = __builtin_bit_cast(uint32_t, pk);
+                asm volatile("" :: "v"(w), "v"(rs));
+                pw[ks][(r & 7) >> 1] = w;
+            };
+            // some row's block maximum exceeds its reference by more than 8
+            // (or sets an unset one)
+            auto over = [&](float ht) {
+                return __builtin_amdgcn_ballot_w64(m2 == -INFINITY ? ht > -INFINITY : ht > 8.f) != 0;
+            };
+            // raise those references to the row maximum, rescaling O and l;
+            // returns the lane's shift of t
+            auto decide = [&](float ht) -> float {
+                const float pt = fmaxf(ht, __shfl_xor(ht, 32));
+                const bool g = (m2 == -INFINITY) ? pt > -INFINITY : pt > 8.f;
+                const float m_new = g ? ((m2 == -INFINITY) ? 0.f : m2) + pt : m2;
+                const float alpha = g ? __builtin_amdgcn_exp2f(m2 - m_new) : 1.f;
+                l_run *= alpha;
+#pragma unroll
+                for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
+                m2 = m_new;
+                return g ? pt : 0.f;
             };
             fr[0] = frag(0);
             fr[1] = frag(1);
@@ -646,52 +674,59 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             }
             if (masked) apply_mask(S0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            // Speculative exps: the exps of a 32-key block use the current
-            // reference while its maximum is still being taken; when the
-            // maximum turns out to exceed the reference by more than 8 (rare;
-            // always on an item's first tile), the block's exps are redone
-            // after the rescale.
-            auto ref_nm = [&]() { return (m_run == -INFINITY) ? 0.f : -m_run * sl2e; };
-            auto over = [&](float hm) { return __builtin_amdgcn_ballot_w64((hm - m_run) * sl2e > 8.f) != 0; };
+            // Speculative exps: a block's exps use the current reference while
+            // its maximum is still being taken; when the maximum exceeds the
+            // reference by more than 8 (rare; always on an item's first
+            // tile), the block's t are shifted and its exps redone after the
+            // rescale.
             float nm = ref_nm();
-            // P2: S1 MFMAs; max and exp of S0
-            float hm = -INFINITY;
+            // P2: S1 MFMAs; t, max and exp of S0
+            float ht = -INFINITY;
 #pragma unroll
             for (int f = 8; f < 16; ++f) {
                 fr[(f + 3) & 3] = frag(f + 3);
                 S1 = E::mma(fr[f & 3], qf[f & 7], S1);
                 const int r = 2 * (f - 8);
-                hm = fmaxf(hm, fmaxf(S0[r], S0[r + 1]));
-                ex2(S0, r >> 3, r, nm);
+                tx(S0, r, nm);
+                ht = max3(ht, S0[r], S0[r + 1]);
+                ex2(S0, r >> 3, r);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (over(hm)) {
-                decide(hm);
-                nm = ref_nm();
+            if (over(ht)) {
+                const float sh = decide(ht);
                 rs = 0.f;
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) ex2(S0, r >> 3, r, nm);
+                for (int r = 0; r < 16; r += 2) {
+                    S0[r] -= sh;
+                    S0[r + 1] -= sh;
+                    ex2(S0, r >> 3, r);
+                }
             }
             l_run += rs;                 // before S1's decision may rescale l
             rs = 0.f;
+            nm = ref_nm();
             if (masked) apply_mask(S1, 1);
             __builtin_amdgcn_sched_barrier(0);
-            // P3: PV of the first half; max of S1 and exp of its registers 0..7
-            hm = -INFINITY;
+            // P3: PV of the first half; t and max of S1, exps of registers 0..7
+            ht = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 fr[(i + 3) & 3] = frag(16 + i + 3);
                 oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
-                hm = fmaxf(hm, fmaxf(S1[2 * i], S1[2 * i + 1]));
-                if (i < 4) ex2(S1, 2, 2 * i, nm);
+                tx(S1, 2 * i, nm);
+                ht = max3(ht, S1[2 * i], S1[2 * i + 1]);
+                if (i < 4) ex2(S1, 2, 2 * i);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (over(hm)) {
-                decide(hm);
-                nm = ref_nm();
+            if (over(ht)) {
+                const float sh = decide(ht);
                 rs = 0.f;
 #pragma unroll
-                for (int r = 0; r < 8; r += 2) ex2(S1, 2, r, nm);
+                for (int r = 0; r < 16; r += 2) {
+                    S1[r] -= sh;
+                    S1[r + 1] -= sh;
+                    if (r < 8) ex2(S1, 2, r);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
             // P4: PV of keys 32..47 under the exp of registers 8..15, then PV
@@ -700,7 +735,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             for (int i = 8; i < 16; ++i) {
                 if (i + 3 < 16) fr[(i + 3) & 3] = frag(16 + i + 3);
                 oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
-                if (i < 12) ex2(S1, 3, 8 + 2 * (i - 8), nm);
+                if (i < 12) ex2(S1, 3, 8 + 2 * (i - 8));
                 __builtin_amdgcn_sched_barrier(0);
             }
             l_run += rs;
@@ -779,6 +814,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float mlog2 = kHandOrdered ? m2 : m_run * sl2e;   // reference in log2 units
     if (!row_ok) return;
     if (nsplit == 1) {
         const float inv = p.v_scale / l_tot;
@@ -803,7 +839,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             }
         }
         if (p.lse && half == 0)
-            p.lse[(size_t)head * p.total_q + q0 + t] = (m_run * sl2e + __log2f(l_tot)) * kLn2;
+            p.lse[(size_t)head * p.total_q + q0 + t] = (mlog2 + __log2f(l_tot)) * kLn2;
     } else {
         const size_t pidx = (size_t)p.seq_info[b].z + ((size_t)split * n + t) * p.num_heads + head;
         float* po = p.part_o + pidx * D;
@@ -818,7 +854,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                 *(f32x4*)(po + d) = v;
             }
         }
-        if (half == 0) p.part_ml[pidx] = make_float2(m_run * sl2e, l_tot);
+        if (half == 0) p.part_ml[pidx] = make_float2(mlog2, l_tot);
     }
 }
 

@@ -30,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -66,11 +67,19 @@ def _args():
     return ap.parse_args()
 
 
+_COMMENT_OR_STRING = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\])*"', re.S)
+
+
 def kernel_sources_sha256() -> str:
+    """Digest of the kernel sources' code: comments dropped and whitespace
+    runs collapsed, so that a recorded counter summary stays valid across
+    edits that cannot change the compiled kernels."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        code = _COMMENT_OR_STRING.sub(lambda m: m.group(0) if m.group(0).startswith('"') else " ", text)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()
 
 

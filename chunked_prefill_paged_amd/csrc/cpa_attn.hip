@@ -566,10 +566,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     // tiles of 32 keys (tiles on the causal diagonal, at a split end or at
     // the sequence end first mask their scores to -inf).  LDS fragments are prefetched three MFMAs ahead through four
     // rotating registers; sched_barrier fences pin the order:
-    //   P1  S0 = K[0:32] Q^T                 (8 MFMAs)
-    //   P2  S1 = K[32:64] Q^T                (8 MFMAs)  || max, exp, sum, convert of S0
-    //   P3  O += V[0:32] P0                  (8 MFMAs)  || max of S1
-    //   P4  O += V[32:64] P1                 (8 MFMAs)  || exp, sum, convert of S1
+    //   P1  S0 = K[0:32] Q^T     (8 MFMAs)
+    //   P2  S1 = K[32:64] Q^T    (8 MFMAs)  || exp2 arguments, max, exp, sum, convert of S0
+    //   P3  O += V[0:32] P0      (8 MFMAs)  || exp2 arguments and max of S1, exps of its keys 32..47
+    //   P4  O += V[32:64] P1     (8 MFMAs)  || exps of keys 48..63 (under the PV of keys 32..47)
     // The reference maximum of a row moves only when some lane's half-row
     // maximum exceeds it by more than 8 (log2 units): the common path needs
     // no exchange between the two lanes of a row; the rare path takes the

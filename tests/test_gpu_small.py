@@ -24,6 +24,12 @@ CASES = [
     ("mixed_decodes", "bf16", 32, 8, 128, 16, 512, [(1300, 1024)], [1, 15, 16, 17, 600, 1111, 2049],
      8192),
     ("tiny_rows", "bf16", 32, 8, 128, 16, 512, [(2, 1), (1, 0), (64, 63)], [], 4096),
+    # head groups that do not divide a 32-row wave block or a 128-row item,
+    # block sizes at and past the 64-key tile and the largest one
+    ("hpg3_bs64", "bf16", 24, 8, 128, 64, 1024, [(777, 640), (100, 0)], [5, 300], 4096),
+    ("hpg6_bs256", "bf16", 48, 8, 128, 256, 1024, [(1000, 512), (300, 0)], [2000], 4096),
+    ("hpg5_d64_bs512", "bf16", 10, 2, 64, 512, 1024, [(1500, 1024)], [700], 4096),
+    ("fp32_hpg3", "fp32", 6, 2, 64, 16, 512, [(300, 200)], [40], 4096),
 ]
 SPLITS = {"auto": (0, 0), "never": (-1, -1), "seg": ("S", "S"), "seg2": ("2S", "S")}
 

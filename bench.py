@@ -50,7 +50,8 @@ def _args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first (the first few dozen run below steady state)")
     ap.add_argument("--kv-segment-size", type=int, default=1024)
     ap.add_argument("--split-keys-prefill", type=int, default=0,
                     help="0 automatic, -1 never, else keys per work item")

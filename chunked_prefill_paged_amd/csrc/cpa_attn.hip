@@ -567,15 +567,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     // the sequence end first mask their scores to -inf).  LDS fragments are prefetched three MFMAs ahead through four
     // rotating registers; sched_barrier fences pin the order:
     //   P1  S0 = K[0:32] Q^T     (8 MFMAs)
-    //   P2  S1 = K[32:64] Q^T    (8 MFMAs)  || exp2 arguments, max, exp, sum, convert of S0
-    //   P3  O += V[0:32] P0      (8 MFMAs)  || exp2 arguments and max of S1, exps of its keys 32..47
+    //   P2  S1 = K[32:64] Q^T    (8 MFMAs)  || exp2 arguments, exp, sum, convert of S0
+    //   P3  O += V[0:32] P0      (8 MFMAs)  || exp2 arguments of S1, exps of its keys 32..47
     //   P4  O += V[32:64] P1     (8 MFMAs)  || exps of keys 48..63 (under the PV of keys 32..47)
-    // The reference maximum of a row moves only when some lane's half-row
-    // maximum exceeds it by more than 8 (log2 units): the common path needs
-    // no exchange between the two lanes of a row; the rare path takes the
-    // row maximum and rescales O and l.  P0's PV is fully issued before S1's
-    // decision, so a rescale covers every product formed under the old
-    // reference.
+    // The reference maximum of a row moves only when the exps of some lane's
+    // share of a block (16 keys of S0, 8 keys of either half of S1) sum past
+    // 2^12 (2^11 for 8 keys), so that one of them exceeds 2^8: the common
+    // path takes no maximum and needs no exchange between the two lanes of a
+    // row, and keeps every exp2 argument <= 12; the rare path takes the row
+    // maximum, raises the reference to it and rescales O and l.  Each share
+    // is checked before its PV is issued and after every PV formed under the
+    // old reference, so a rescale covers exactly those products.
     constexpr bool kHandOrdered = (KPL == 8 && D == 128);
     // LDS byte offsets of this lane's fragments: K fragment (k-step s8,
     // 32-key block sb) at k_base + ((s8*16) ^ k_x) + sb*32*D*2; V fragment
@@ -616,8 +618,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             };
             // Scores become exp2 arguments t = S * scale * log2(e) - m2 in
             // place (m2: the row's reference maximum in log2 units, taken as
-            // 0 while unset).  The block maximum is taken on t: fma results
-            // need no NaN quieting, so one v_max3 folds two scores.
+            // 0 while unset).  The rare path's maximum is taken on t: fma
+            // results need no NaN quieting, so one v_max3 folds two scores.
             auto ref_nm = [&]() { return (m2 == -INFINITY) ? 0.f : -m2; };
             // one v_max3 per score pair, chained (the compiler otherwise
             // builds a tree of two-input maxima)
@@ -643,10 +645,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                 asm volatile("" :: "v"(w), "v"(rs));
                 pw[ks][(r & 7) >> 1] = w;
             };
-            // some row's block maximum exceeds its reference by more than 8
-            // (or sets an unset one)
-            auto over = [&](float ht) {
-                return __builtin_amdgcn_ballot_w64(m2 == -INFINITY ? ht > -INFINITY : ht > 8.f) != 0;
+            // some lane's n exps of one share sum past cap = n * 2^8 (so one
+            // of them has t > 8), or some row of the wave has no reference
+            auto over = [&](float sum, float cap) {
+                return __builtin_amdgcn_ballot_w64(m2 == -INFINITY || sum > cap) != 0;
+            };
+            // the lane's maximum t over registers [r0, 16) of a block
+            auto tmax = [&](const f32x16& S, int r0) {
+                float ht = -INFINITY;
+#pragma unroll
+                for (int r = r0; r < 16; r += 2) ht = max3(ht, S[r], S[r + 1]);
+                return ht;
             };
             // raise those references to the row maximum, rescaling O and l;
             // returns the lane's shift of t
@@ -674,26 +683,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             }
             if (masked) apply_mask(S0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            // Speculative exps: a block's exps use the current reference while
-            // its maximum is still being taken; when the maximum exceeds the
-            // reference by more than 8 (rare; always on an item's first
-            // tile), the block's t are shifted and its exps redone after the
-            // rescale.
+            // Speculative exps: a block's exps use the current reference
+            // before the block is checked; when the check fails (rare; always
+            // while some row of the wave has no reference, as on an item's
+            // first tile), the block's t are shifted and its exps redone
+            // after the rescale.
             float nm = ref_nm();
-            // P2: S1 MFMAs; t, max and exp of S0
-            float ht = -INFINITY;
+            // P2: S1 MFMAs; t and exp of S0
 #pragma unroll
             for (int f = 8; f < 16; ++f) {
                 fr[(f + 3) & 3] = frag(f + 3);
                 S1 = E::mma(fr[f & 3], qf[f & 7], S1);
                 const int r = 2 * (f - 8);
                 tx(S0, r, nm);
-                ht = max3(ht, S0[r], S0[r + 1]);
                 ex2(S0, r >> 3, r);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (over(ht)) {
-                const float sh = decide(ht);
+            if (over(rs, 4096.f)) {
+                const float sh = decide(tmax(S0, 0));
                 rs = 0.f;
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
@@ -707,19 +714,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             nm = ref_nm();
             if (masked) apply_mask(S1, 1);
             __builtin_amdgcn_sched_barrier(0);
-            // P3: PV of the first half; t and max of S1, exps of registers 0..7
-            ht = -INFINITY;
+            // P3: PV of the first half; t of S1, exps of registers 0..7
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 fr[(i + 3) & 3] = frag(16 + i + 3);
                 oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
                 tx(S1, 2 * i, nm);
-                ht = max3(ht, S1[2 * i], S1[2 * i + 1]);
                 if (i < 4) ex2(S1, 2, 2 * i);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (over(ht)) {
-                const float sh = decide(ht);
+            if (over(rs, 2048.f)) {
+                const float sh = decide(tmax(S1, 0));
                 rs = 0.f;
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
@@ -728,14 +733,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                     if (r < 8) ex2(S1, 2, r);
                 }
             }
+            l_run += rs;                 // before the second decision may rescale l
+            rs = 0.f;
             __builtin_amdgcn_sched_barrier(0);
-            // P4: PV of keys 32..47 under the exp of registers 8..15, then PV
-            // of keys 48..63
+            // P4: PV of keys 32..47 under the exp of registers 8..15, then
+            // (after their own check) PV of keys 48..63
 #pragma unroll
-            for (int i = 8; i < 16; ++i) {
+            for (int i = 8; i < 12; ++i) {
+                fr[(i + 3) & 3] = frag(16 + i + 3);
+                oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
+                ex2(S1, 3, 8 + 2 * (i - 8));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (over(rs, 2048.f)) {
+                const float sh = decide(tmax(S1, 8));
+                rs = 0.f;
+#pragma unroll
+                for (int r = 8; r < 16; r += 2) {
+                    S1[r] -= sh;
+                    S1[r + 1] -= sh;
+                    ex2(S1, 3, r);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 12; i < 16; ++i) {
                 if (i + 3 < 16) fr[(i + 3) & 3] = frag(16 + i + 3);
                 oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
-                if (i < 12) ex2(S1, 3, 8 + 2 * (i - 8));
                 __builtin_amdgcn_sched_barrier(0);
             }
             l_run += rs;

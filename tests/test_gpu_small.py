@@ -157,6 +157,39 @@ def test_selector_queries_select_exact_value_rows():
     assert len(hit) == -(-L // bs)
 
 
+@pytest.mark.parametrize("split", [-1, 512], ids=["unsplit", "split512"])
+def test_growing_scores_move_the_reference(split):
+    """Scores that climb along the keys, by a slow ramp and by jumps placed at
+    key offsets 5, 20, 35, 40, 55 and 60 of their 64-key tiles (each of the
+    first 32, the next 16 and the last 16 keys of a tile), so that the
+    running reference of the online softmax moves many times per row and at
+    every point of a tile where the kernel may move it."""
+    need_gpu()
+    H, G, D, bs, S = 32, 8, 128, 16, 512
+    rng = np.random.default_rng(11)
+    computed, n = 2000, 600
+    L = computed + n
+    u = rng.standard_normal((G, D))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    jumps = [64 * m + r for m, r in ((4, 5), (11, 40), (17, 55), (23, 20), (32, 60), (37, 35))]
+    ramp = 0.01 * np.arange(L) + 8.0 * np.searchsorted(jumps, np.arange(L), side="right")
+    k = 0.5 * rng.standard_normal((L, G, D)) + ramp[:, None, None] * u[None]
+    kt, k64 = quantize(k, "bf16")
+    vt, v64 = quantize(rng.standard_normal((L, G, D)), "bf16")
+    nb = -(-L // bs) + 20
+    pair = Pair(nb, G, bs, D, "bf16", 4096, -(-L // bs) + 1, rng.permutation(nb).astype(np.int32))
+    pair.add_partial(0, L, computed)
+    pair.fill_context(0, k64[:computed], v64[:computed], kt[:computed], vt[:computed])
+    pb, ob = pair.step()
+    alpha = rng.uniform(8.0, 14.0, H)
+    q = 0.3 * rng.standard_normal((n, H, D)) + alpha[None, :, None] * u[np.arange(H) // (H // G)][None]
+    qt, q64 = quantize(q, "bf16")
+    say(f"growing scores split={split}")
+    out, _ = gpu_call(pair.cache, pb, qt, kt[computed:], vt[computed:], S, split_pre=split)
+    ref = pair.oracle_batch(ob, q64, k64[computed:], v64[computed:], 1 / math.sqrt(D), G)
+    assert_close(out.to(torch.float64).numpy(), ref, "bf16", f"growing/{split}")
+
+
 def test_empty_sequence_in_batch_and_lse():
     """A batch with a zero-length sequence between two real ones; the optional
     log-sum-exp output matches the closed form for K = 0 (log of the number of

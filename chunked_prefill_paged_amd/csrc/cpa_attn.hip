@@ -566,10 +566,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     // tiles of 32 keys (tiles on the causal diagonal, at a split end or at
     // the sequence end first mask their scores to -inf).  LDS fragments are prefetched three MFMAs ahead through four
     // rotating registers; sched_barrier fences pin the order:
-    //   P1  S0 = K[0:32] Q^T     (8 MFMAs)
-    //   P2  S1 = K[32:64] Q^T    (8 MFMAs)  || exp2 arguments, exp, sum, convert of S0
-    //   P3  O += V[0:32] P0      (8 MFMAs)  || exp2 arguments of S1, exps of its keys 32..47
-    //   P4  O += V[32:64] P1     (8 MFMAs)  || exps of keys 48..63 (under the PV of keys 32..47)
+    //   P1  S0 = K[0:32] Q^T - m2   (8 MFMAs)
+    //   P2  S1 = K[32:64] Q^T - m2  (8 MFMAs)  || exp, sum, convert of S0
+    //   P3  O += V[0:32] P0         (8 MFMAs)  || exps of S1's keys 32..47
+    //   P4  O += V[32:64] P1        (8 MFMAs)  || exps of keys 48..63 (under the PV of keys
+    //                                              32..47), then the next tile's -m2 presets
     // The reference maximum of a row moves only when the exps of some lane's
     // share of a block (16 keys of S0, 8 keys of either half of S1) sum past
     // 2^12 (2^11 for 8 keys), so that one of them exceeds 2^8: the common
@@ -590,6 +591,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
         v_base = (uint32_t)(lrow * kKeys * 2 + (half ^ (swl & 1)) * 16);
         v_x = (uint32_t)((swl & 6) * 16);
     }
+    // The hand-ordered path's score accumulators: each QK chain starts from
+    // -m2 (set for the next tile once a tile's last check has passed), and
+    // the queries carry scale * log2(e), so the MFMAs leave the exp2
+    // arguments t = S * scale * log2(e) - m2 themselves.
+    f32x16 S0 = {}, S1 = {};
     auto compute_tile = [&](int buf, int ts, bool masked) {
         if constexpr (kHandOrdered) {
             typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -603,7 +609,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             };
             // fragment j of the tile's 32 LDS reads: K fragments 0..15, then V 0..15
             auto frag = [&](int j) { return j < 16 ? kfrag(j) : vfrag(j - 16); };
-            f32x16 S0 = {}, S1 = {};
             bf16x8 fr[4];
             u32x4 pw[4];
             float rs = 0.f;
@@ -616,10 +621,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                     if (j > lim || j >= k1) S[r] = -INFINITY;
                 }
             };
-            // Scores become exp2 arguments t = S * scale * log2(e) - m2 in
-            // place (m2: the row's reference maximum in log2 units, taken as
-            // 0 while unset).  The rare path's maximum is taken on t: fma
-            // results need no NaN quieting, so one v_max3 folds two scores.
+            // S0 and S1 hold exp2 arguments t = S * scale * log2(e) - m2 (m2:
+            // the row's reference maximum in log2 units, taken as 0 while
+            // unset).  The rare path's maximum is taken on t: MFMA results
+            // need no NaN quieting here, so one v_max3 folds two scores.
             auto ref_nm = [&]() { return (m2 == -INFINITY) ? 0.f : -m2; };
             // one v_max3 per score pair, chained (the compiler otherwise
             // builds a tree of two-input maxima)
@@ -627,10 +632,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                 float d;
                 asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
                 return d;
-            };
-            auto tx = [&](f32x16& S, int r, float nm) {
-                S[r] = __builtin_fmaf(S[r], sl2e, nm);
-                S[r + 1] = __builtin_fmaf(S[r + 1], sl2e, nm);
             };
             // exp/sum/convert of registers r, r+1 of t into pw (the empty
             // asm consumes the results where they are computed: a
@@ -688,14 +689,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             // while some row of the wave has no reference, as on an item's
             // first tile), the block's t are shifted and its exps redone
             // after the rescale.
-            float nm = ref_nm();
-            // P2: S1 MFMAs; t and exp of S0
+            // P2: S1 MFMAs; exps of S0
 #pragma unroll
             for (int f = 8; f < 16; ++f) {
                 fr[(f + 3) & 3] = frag(f + 3);
                 S1 = E::mma(fr[f & 3], qf[f & 7], S1);
                 const int r = 2 * (f - 8);
-                tx(S0, r, nm);
                 ex2(S0, r >> 3, r);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -708,18 +707,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                     S0[r + 1] -= sh;
                     ex2(S0, r >> 3, r);
                 }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) S1[r] -= sh;   // started from the old -m2 too
             }
             l_run += rs;                 // before S1's decision may rescale l
             rs = 0.f;
-            nm = ref_nm();
             if (masked) apply_mask(S1, 1);
             __builtin_amdgcn_sched_barrier(0);
-            // P3: PV of the first half; t of S1, exps of registers 0..7
+            // P3: PV of the first half; exps of S1's registers 0..7
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 fr[(i + 3) & 3] = frag(16 + i + 3);
                 oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
-                tx(S1, 2 * i, nm);
                 if (i < 4) ex2(S1, 2, 2 * i);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -756,12 +755,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
+            // the reference is final for this tile: preset the next tile's
+            // accumulators under the last PV
+            // (as pairs: one 64-bit move sets two registers)
+            typedef uint64_t u64x8 __attribute__((ext_vector_type(8)));
+            const uint64_t nb = __builtin_bit_cast(uint32_t, ref_nm());
+            const uint64_t n2 = (nb << 32) | nb;
+            u64x8 z0 = __builtin_bit_cast(u64x8, S0), z1 = __builtin_bit_cast(u64x8, S1);
 #pragma unroll
             for (int i = 12; i < 16; ++i) {
                 if (i + 3 < 16) fr[(i + 3) & 3] = frag(16 + i + 3);
                 oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
+#pragma unroll
+                for (int j = 2 * (i - 12); j < 2 * (i - 11); ++j) {
+                    uint64_t x0, x1;
+                    asm volatile("v_mov_b64 %0, %1" : "=v"(x0) : "v"(n2));
+                    asm volatile("v_mov_b64 %0, %1" : "=v"(x1) : "v"(n2));
+                    z0[j] = x0;
+                    z1[j] = x1;
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            S0 = __builtin_bit_cast(f32x16, z0);
+            S1 = __builtin_bit_cast(f32x16, z1);
             l_run += rs;
         }
     };
@@ -797,6 +813,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             if (nfull > 1) btn = load_bt(tstart(1));
         }
         wait_vmem();                     // Q and the first block ids
+        if constexpr (kHandOrdered) {
+            // queries times scale * log2(e), rounded to bf16 once per item
+#pragma unroll
+            for (int f = 0; f < NQF; ++f) {
+#pragma unroll
+                for (int e = 0; e < KPL; ++e) qf[f][e] = (T)((float)qf[f][e] * sl2e);
+            }
+        }
         for (int u = 0; u < ntiles; ++u) {
             const int ts = tstart(u);
             const int buf = u & 1;

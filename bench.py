@@ -50,7 +50,7 @@ def _args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=30,
+    ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first (the first few dozen run below steady state)")
     ap.add_argument("--kv-segment-size", type=int, default=1024)
     ap.add_argument("--split-keys-prefill", type=int, default=0,
@@ -285,7 +285,7 @@ def run_long_prompt(args):
     bench = PromptBench(S, args.split_keys_prefill, workload="c5", kv_fp8=args.kv_cache == "fp8")
     w = bench.w
     steps = max(1, min(args.steps, 5))
-    warm = max(1, min(args.warmup, 2))
+    warm = max(1, min(args.warmup, 10))
     for _ in range(warm):
         bench.step()
     torch.cuda.synchronize()

@@ -150,26 +150,33 @@ class PromptBench:
         self.rid = 0
         # chunk plan of the prompt (fixed): build one call per chunk index with
         # persistent device descriptor buffers and pinned host staging
-        from chunked_prefill_paged_amd import schedule_prompt
+        from chunked_prefill_paged_amd import INLINE_DESC_INTS, schedule_prompt
         self.chunks = schedule_prompt(w.max_batched_tokens, 0, w.prompt_len)
         self.calls, self.dev_desc, self.pinned, self.copied = [], [], [], []
+        # the per-chunk descriptor (cu_seqlens_q, cached_seq_len, block-table
+        # row) rides in the launches' arguments when it fits; otherwise it
+        # is uploaded with one copy from pinned memory.  No slot mapping:
+        # the library derives the slots from the block table.
+        n32 = 2 + 1 + self.max_blocks
+        self.inline = n32 <= INLINE_DESC_INTS
         pos = 0
         ws_bytes = 256
         for n in self.chunks:
-            # one int32 descriptor per chunk (cu_seqlens_q, cached_seq_len,
-            # block-table row), uploaded with one copy; no slot mapping: the
-            # library derives the slots from the block table
-            n32 = 2 + 1 + self.max_blocks
-            d_i32 = torch.zeros(n32, dtype=torch.int32, device=dev)
-            p_i32 = torch.zeros(n32, dtype=torch.int32, pin_memory=True)
+            if self.inline:
+                d_i32 = p_i32 = None
+                dev_desc = dict(cu_seqlens_q=None, cached_seq_len=None, block_table=None,
+                                h_block_table=np.zeros((1, self.max_blocks), np.int32))
+            else:
+                d_i32 = torch.zeros(n32, dtype=torch.int32, device=dev)
+                p_i32 = torch.zeros(n32, dtype=torch.int32, pin_memory=True)
+                dev_desc = dict(cu_seqlens_q=d_i32[0:2], cached_seq_len=d_i32[2:3],
+                                block_table=d_i32[3:].view(1, self.max_blocks))
             call = AttnCall(q=self.q[pos:pos + n], k_new=self.k[pos:pos + n], v_new=self.v[pos:pos + n],
                             k_cache=self.k_cache, v_cache=self.v_cache, out=self.out[pos:pos + n],
-                            cu_seqlens_q=d_i32[0:2], cached_seq_len=d_i32[2:3],
-                            block_table=d_i32[3:].view(1, self.max_blocks), slot_mapping=None,
-                            h_cu_seqlens_q=np.array([0, n], np.int32),
+                            slot_mapping=None, h_cu_seqlens_q=np.array([0, n], np.int32),
                             h_cached_seq_len=np.array([pos], np.int32),
                             kv_segment_size=kv_segment_size, split_keys_prefill=split_pre,
-                            k_scale=FP8_SCALE, v_scale=FP8_SCALE)
+                            k_scale=FP8_SCALE, v_scale=FP8_SCALE, **dev_desc)
             ws_bytes = max(ws_bytes, call.workspace_bytes())
             self.calls.append(call)
             self.dev_desc.append(d_i32)
@@ -197,20 +204,25 @@ class PromptBench:
         sched.add_request(self.rid, self.w.prompt_len)
         for i, call in enumerate(self.calls):
             b = sched.step()
-            p_i32 = self.pinned[i]
-            if self.copied[i] is not None:
-                self.copied[i].synchronize()        # staging buffer of the previous step is free
-            a32 = p_i32.numpy()
-            a32[0:2] = b["cu_seqlens_q"]
-            a32[2] = b["cached_seq_len"][0]
-            a32[3:] = b["block_table"][0]
-            self.dev_desc[i].copy_(p_i32, non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record()
-            self.copied[i] = ev
+            if self.inline:
+                bt = np.ascontiguousarray(b["block_table"], dtype=np.int32)
+                call.args.h_block_table = bt.ctypes.data
+            else:
+                bt = None
+                p_i32 = self.pinned[i]
+                if self.copied[i] is not None:
+                    self.copied[i].synchronize()    # staging buffer of the previous step is free
+                a32 = p_i32.numpy()
+                a32[0:2] = b["cu_seqlens_q"]
+                a32[2] = b["cached_seq_len"][0]
+                a32[3:] = b["block_table"][0]
+                self.dev_desc[i].copy_(p_i32, non_blocking=True)
+                ev = torch.cuda.Event()
+                ev.record()
+                self.copied[i] = ev
             call.args.h_cu_seqlens_q = b["cu_seqlens_q"].ctypes.data
             call.args.h_cached_seq_len = b["cached_seq_len"].ctypes.data
-            call._keep_host = (b["cu_seqlens_q"], b["cached_seq_len"])
+            call._keep_host = (b["cu_seqlens_q"], b["cached_seq_len"], bt)
             call.prepare()
             if events is not None:
                 events[i][0].record()

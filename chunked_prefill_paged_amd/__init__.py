@@ -7,5 +7,5 @@ its thin Python binding.  Nothing falls back to Python or PyTorch compute: if
 the library is missing, every entry point raises.
 """
 from ._lib import BudgetExhausted, CpaError, OutOfBlocks, lib  # noqa: F401
-from .attention import AttnCall, cache_shapes  # noqa: F401
+from .attention import INLINE_DESC_INTS, AttnCall, cache_shapes  # noqa: F401
 from .scheduler import HostScheduler, schedule_prompt  # noqa: F401

@@ -20,6 +20,7 @@ CPA_ERR_OUT_OF_BLOCKS = 4
 CPA_ERR_HIP = 5
 CPA_ERR_WORKSPACE = 6
 CPA_ERR_NOT_FOUND = 7
+CPA_INLINE_DESC_INTS = 896      # largest batch descriptor the launches take inline (int32s)
 
 CPA_BF16 = 0
 CPA_FP32 = 1
@@ -44,6 +45,7 @@ class AttnArgs(ctypes.Structure):
         ("slot_mapping", _vp), ("out", _vp), ("lse", _vp), ("workspace", _vp),
         ("workspace_bytes", ctypes.c_size_t), ("h_cu_seqlens_q", _vp), ("h_cached_seq_len", _vp),
         ("kv_dtype", _i32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+        ("h_block_table", _vp),
     ]
 
 

@@ -52,6 +52,9 @@ def cache_shapes(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: 
             (num_blocks, num_kv_heads, head_dim, block_size))
 
 
+INLINE_DESC_INTS = _lib.CPA_INLINE_DESC_INTS
+
+
 class AttnCall:
     """One batch's attention metadata bound to its tensors."""
 
@@ -59,10 +62,14 @@ class AttnCall:
                  cached_seq_len, block_table, slot_mapping, h_cu_seqlens_q,
                  h_cached_seq_len, kv_segment_size, scale=None, lse=None, workspace=None,
                  decode_token_threshold=0, split_keys_prefill=0, split_keys_decode=0,
-                 k_scale=1.0, v_scale=1.0):
+                 k_scale=1.0, v_scale=1.0, h_block_table=None):
         """A cache of one-byte elements (uint8 or float8_e4m3fn) holds E4M3
         codes under per-tensor scales ``k_scale`` / ``v_scale``; the other
-        tensors are then bfloat16."""
+        tensors are then bfloat16.  ``h_block_table`` (host int32 [num_seqs,
+        max_blocks]) lets the launches carry the batch descriptor in their
+        own arguments when it fits ``INLINE_DESC_INTS``; the device
+        ``cu_seqlens_q``, ``cached_seq_len`` and ``block_table`` may then be
+        None."""
         num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
         if tuple(v_cache.shape) != (num_blocks, num_kv_heads, head_dim, block_size):
             raise ValueError(f"v_cache must be {(num_blocks, num_kv_heads, head_dim, block_size)}")
@@ -70,8 +77,11 @@ class AttnCall:
         num_heads = q.shape[1] if q is not None else num_kv_heads
         h_cu = np.ascontiguousarray(h_cu_seqlens_q, dtype=np.int32)
         h_cached = np.ascontiguousarray(h_cached_seq_len, dtype=np.int32)
+        h_bt = None if h_block_table is None else np.ascontiguousarray(h_block_table, dtype=np.int32)
+        if h_bt is not None and (h_bt.ndim != 2 or h_bt.shape[0] != len(h_cu) - 1):
+            raise ValueError("h_block_table must be [num_seqs, max_blocks]")
         self._keep = [q, k_new, v_new, k_cache, v_cache, out, cu_seqlens_q, cached_seq_len,
-                      block_table, slot_mapping, lse, h_cu, h_cached]
+                      block_table, slot_mapping, lse, h_cu, h_cached, h_bt]
         for t in (cu_seqlens_q, cached_seq_len, block_table):
             if t is not None and str(t.dtype) != "torch.int32":
                 raise TypeError("cu_seqlens_q, cached_seq_len and block_table must be int32")
@@ -91,7 +101,8 @@ class AttnCall:
         a.head_dim = head_dim
         a.block_size = block_size
         a.kv_segment_size = kv_segment_size
-        a.max_blocks_per_seq = block_table.shape[1] if block_table is not None else 1
+        a.max_blocks_per_seq = (block_table.shape[1] if block_table is not None
+                                else h_bt.shape[1] if h_bt is not None else 1)
         a.num_blocks = num_blocks
         a.decode_token_threshold = decode_token_threshold
         a.split_keys_prefill = split_keys_prefill
@@ -104,6 +115,7 @@ class AttnCall:
         a.out, a.lse = _ptr(out), _ptr(lse)
         a.h_cu_seqlens_q = h_cu.ctypes.data
         a.h_cached_seq_len = h_cached.ctypes.data
+        a.h_block_table = h_bt.ctypes.data if h_bt is not None else None
         self.args = a
         if workspace is not None:
             self.set_workspace(workspace)

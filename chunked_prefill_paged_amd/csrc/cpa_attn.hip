@@ -1010,6 +1010,16 @@ struct PrepParams {
     int4* items;
     int2* merge;
     int32_t* header;
+    // inline descriptor: its length, and (with a plan) where the workspace
+    // copy for the attention launch goes
+    int32_t desc_len;
+    int32_t* desc_out;
+};
+
+// cu_seqlens_q [B + 1], cached_seq_len [B] and the block table [B, max_blocks],
+// passed by value as a kernel argument
+struct InlineDesc {
+    int32_t v[kInlineDescInts];
 };
 
 constexpr int kPlanSmem = (3 * kMaxSeqs + 2) * 4 + kMaxSeqs * 2;
@@ -1383,8 +1393,7 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
 // Grid: cache_wgs cache-write workgroups, then (with ROPE) rope_wgs
 // query-rotation workgroups, then (with a plan) one plan builder.
 template <typename T, int D, bool ROPE, bool FP8>
-__global__ __launch_bounds__(kThreads) void prep_kernel(const PrepParams p) {
-    __shared__ __attribute__((aligned(16))) char smem[kPrepSmem];
+__device__ void prep_body(const PrepParams& p, char* smem) {
     const int wg = blockIdx.x;
     if (wg < p.cache_wgs) {
         cache_write<T, D, ROPE, FP8>(p, smem);
@@ -1397,6 +1406,28 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(const PrepParams p) {
         }
     }
     build_plan(p, smem);
+}
+
+template <typename T, int D, bool ROPE, bool FP8>
+__global__ __launch_bounds__(kThreads) void prep_kernel(const PrepParams p) {
+    __shared__ __attribute__((aligned(16))) char smem[kPrepSmem];
+    prep_body<T, D, ROPE, FP8>(p, smem);
+}
+
+// The same with the batch descriptor in the kernel arguments: every
+// workgroup reads it there, and the plan builder also leaves a copy in the
+// workspace for the attention launch.
+template <typename T, int D, bool ROPE, bool FP8>
+__global__ __launch_bounds__(kThreads) void prep_kernel_inline(const PrepParams p0, const InlineDesc d) {
+    __shared__ __attribute__((aligned(16))) char smem[kPrepSmem];
+    PrepParams p = p0;
+    p.cu = d.v;
+    p.cached = d.v + p.num_seqs + 1;
+    p.block_table = d.v + 2 * p.num_seqs + 1;
+    if (p.plan && blockIdx.x == gridDim.x - 1) {
+        for (int i = threadIdx.x; i < p.desc_len; i += kThreads) p.desc_out[i] = d.v[i];
+    }
+    prep_body<T, D, ROPE, FP8>(p, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1486,22 +1517,38 @@ cpa_status resolve(const cpa_attn_args* a, Resolved* r) {
     return CPA_OK;
 }
 
+static_assert(kInlineDescInts == CPA_INLINE_DESC_INTS, "inline descriptor size");
+
+// int32 values of the batch descriptor: cu_seqlens_q, cached_seq_len, block table
+inline int64_t desc_ints(const cpa_attn_args* a) {
+    return 2 * (int64_t)a->num_seqs + 1 + (int64_t)a->num_seqs * a->max_blocks_per_seq;
+}
+// the descriptor travels in the launches' arguments (host copies given, small enough)
+inline bool inline_desc(const cpa_attn_args* a) {
+    return a->h_block_table && a->h_cu_seqlens_q && a->h_cached_seq_len && a->num_seqs > 0 &&
+           a->max_blocks_per_seq > 0 && desc_ints(a) <= kInlineDescInts;
+}
+// device copies of the descriptor, or NULL where they may be absent
+inline bool have_desc(const cpa_attn_args* a) {
+    return inline_desc(a) || (a->cu_seqlens_q && a->cached_seq_len && a->block_table);
+}
+
 cpa_status check_pointers(const cpa_attn_args* a, bool attention) {
     if (a->total_q > 0 && (!a->k_new || !a->v_new)) return CPA_ERR_INVALID_ARG;
     // without a slot mapping, slots come from the block table
     if (a->total_q > 0 && !a->slot_mapping &&
-        (!a->cu_seqlens_q || !a->cached_seq_len || !a->block_table || a->num_seqs <= 0 ||
-         a->max_blocks_per_seq <= 0))
+        (!have_desc(a) || a->num_seqs <= 0 || a->max_blocks_per_seq <= 0))
         return CPA_ERR_INVALID_ARG;
     if (!a->k_cache || !a->v_cache) return CPA_ERR_INVALID_ARG;
     if (attention) {
         if (a->total_q > 0 && (!a->q || !a->out)) return CPA_ERR_INVALID_ARG;
-        if (!a->cu_seqlens_q || !a->cached_seq_len || !a->block_table) return CPA_ERR_INVALID_ARG;
+        if (!have_desc(a)) return CPA_ERR_INVALID_ARG;
     }
     return CPA_OK;
 }
 
 inline bool kv_fp8(const cpa_attn_args* a) { return a->kv_dtype == CPA_FP8_E4M3; }
+
 inline float scale_or_one(float s) { return s == 0.f ? 1.f : s; }
 
 template <typename T, int D, bool FP8>
@@ -1556,9 +1603,30 @@ cpa_status launch_prep(const cpa_attn_args* a, const Resolved* r, bool plan, con
     if (grid == 0) return CPA_OK;
     if constexpr (FP8) {
         if (rope) return CPA_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL((prep_kernel<T, D, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    }
+    if (inline_desc(a)) {
+        // the host copies go into the launch's own arguments
+        InlineDesc d;
+        const int B = a->num_seqs;
+        const int64_t nbt = (int64_t)B * a->max_blocks_per_seq;
+        std::memcpy(d.v, a->h_cu_seqlens_q, (size_t)(B + 1) * 4);
+        std::memcpy(d.v + B + 1, a->h_cached_seq_len, (size_t)B * 4);
+        std::memcpy(d.v + 2 * B + 1, a->h_block_table, (size_t)nbt * 4);
+        p.desc_len = (int32_t)desc_ints(a);
+        p.desc_out = plan ? (int32_t*)((char*)a->workspace + r->ws.desc) : nullptr;
+        if constexpr (FP8)
+            hipLaunchKernelGGL((prep_kernel_inline<T, D, false, true>), dim3(grid), dim3(kThreads), 0, stream,
+                               p, d);
+        else if (rope)
+            hipLaunchKernelGGL((prep_kernel_inline<T, D, true, false>), dim3(grid), dim3(kThreads), 0, stream,
+                               p, d);
+        else
+            hipLaunchKernelGGL((prep_kernel_inline<T, D, false, false>), dim3(grid), dim3(kThreads), 0,
+                               stream, p, d);
     } else {
-        if (rope)
+        if constexpr (FP8)
+            hipLaunchKernelGGL((prep_kernel<T, D, false, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+        else if (rope)
             hipLaunchKernelGGL((prep_kernel<T, D, true, false>), dim3(grid), dim3(kThreads), 0, stream, p);
         else
             hipLaunchKernelGGL((prep_kernel<T, D, false, false>), dim3(grid), dim3(kThreads), 0, stream, p);
@@ -1579,6 +1647,12 @@ cpa_status launch_attention(const cpa_attn_args* a, const Resolved* r, hipStream
         p.cu = a->cu_seqlens_q;
         p.cached = a->cached_seq_len;
         p.block_table = a->block_table;
+        if (inline_desc(a)) {           // the copy the prepare launch left
+            const int32_t* dw = (const int32_t*)(ws + r->ws.desc);
+            p.cu = dw;
+            p.cached = dw + a->num_seqs + 1;
+            p.block_table = dw + 2 * a->num_seqs + 1;
+        }
         p.seq_info = (const int4*)(ws + r->ws.seq_info);
         p.items = (const int4*)(ws + r->ws.items);
         p.part_ml = (float2*)(ws + r->ws.part_ml);
@@ -1603,7 +1677,7 @@ cpa_status launch_attention(const cpa_attn_args* a, const Resolved* r, hipStream
     }
     if (r->merge > 0) {
         MergeParams m{};
-        m.cu = a->cu_seqlens_q;
+        m.cu = inline_desc(a) ? (const int32_t*)(ws + r->ws.desc) : a->cu_seqlens_q;
         m.seq_info = (const int4*)(ws + r->ws.seq_info);
         m.merge = (const int2*)(ws + r->ws.merge);
         m.part_ml = (const float2*)(ws + r->ws.part_ml);
@@ -1646,8 +1720,8 @@ cpa_status check_rope(const cpa_attn_args* a, const cpa_rope_args* rope) {
     if (!std::isfinite(rope->theta) || !(rope->theta > 0.f)) return CPA_ERR_INVALID_ARG;
     if (rope->interleaved != 0 && rope->interleaved != 1) return CPA_ERR_INVALID_ARG;
     if (a->num_heads <= 0 || a->num_heads % a->num_kv_heads != 0) return CPA_ERR_INVALID_ARG;
-    if (a->total_q > 0 && (!a->q || !rope->q_out || !a->cu_seqlens_q || !a->cached_seq_len ||
-                           a->num_seqs <= 0))
+    if (a->total_q > 0 && (!a->q || !rope->q_out || a->num_seqs <= 0 ||
+                           (!inline_desc(a) && (!a->cu_seqlens_q || !a->cached_seq_len))))
         return CPA_ERR_INVALID_ARG;
     return CPA_OK;
 }

@@ -28,6 +28,7 @@ namespace cpa {
 constexpr int kRows = 128;            // rows per work item (4 waves x 32)
 constexpr int kMaxSeqs = 4096;        // sequences per call (plan held in LDS)
 constexpr int kNoSplit = 0x7fffffff;  // keys per item when a row is not split
+constexpr int kInlineDescInts = 896;  // cu, cached and block table passed inline (int32s)
 
 struct SeqPlan {
     int32_t tiles;    // row tiles
@@ -65,6 +66,7 @@ struct WsLayout {
     size_t merge;      // int2 [num_merge]: b, t
     size_t part_ml;    // float2 [num_parts]: m (log2 units), l
     size_t part_o;     // float [num_parts, D]: unnormalised output
+    size_t desc;       // int32 [kInlineDescInts]: cu, cached, block table (inline uploads)
     size_t total;
 };
 
@@ -79,6 +81,7 @@ CPA_HD inline WsLayout ws_layout(int32_t num_seqs, int64_t items, int64_t merge,
     w.merge = off;     off = align256(off + (size_t)merge * 8);
     w.part_ml = off;   off = align256(off + (size_t)parts * 8);
     w.part_o = off;    off = align256(off + (size_t)parts * head_dim * 4);
+    w.desc = off;      off = align256(off + (size_t)kInlineDescInts * 4);
     w.total = off;
     return w;
 }

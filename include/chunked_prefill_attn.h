@@ -59,7 +59,11 @@
 extern "C" {
 #endif
 
-#define CPA_ABI_VERSION 2
+#define CPA_ABI_VERSION 3
+
+/* Largest batch descriptor (2 * num_seqs + 1 + num_seqs * max_blocks_per_seq
+ * int32 values) that cpa_prepare can take inline from host copies. */
+#define CPA_INLINE_DESC_INTS 896
 
 typedef enum cpa_status {
     CPA_OK = 0,
@@ -129,6 +133,16 @@ typedef struct cpa_attn_args {
     int32_t kv_dtype;
     float   k_scale;                /* fp8 cache: K scale, > 0 (0 means 1)     */
     float   v_scale;                /* fp8 cache: V scale, > 0 (0 means 1)     */
+    /* Host copy of block_table (num_seqs rows of max_blocks_per_seq), or
+     * NULL.  When it is given and the descriptor fits CPA_INLINE_DESC_INTS,
+     * the launches take cu_seqlens_q, cached_seq_len and the block table
+     * from the host copies, read at the call (no separate upload): the
+     * prepare launch carries them as kernel arguments and leaves a copy in
+     * the workspace, which cpa_attention then reads.  The device arrays are
+     * not read and may be NULL; cpa_prepare and cpa_attention of one batch
+     * must then both be given the host copies.  A larger descriptor needs
+     * the device arrays, as does a NULL h_block_table. */
+    const int32_t* h_block_table;
 } cpa_attn_args;
 
 /* Work decomposition the library derives from the host mirrors. */

@@ -83,21 +83,30 @@ def _dev(a, dt):
 
 
 def gpu_call(cache, batch, q, k_new, v_new, kv_segment_size, *, scale=None, want_lse=False,
-             split_pre=0, split_dec=0, dec_thresh=0, only_cache=False, derive_slots=False):
+             split_pre=0, split_dec=0, dec_thresh=0, only_cache=False, derive_slots=False,
+             inline_desc=False, attention_twice=False):
     """Run one batch through the library.  q/k_new/v_new are CPU or device
     tensors of the cache dtype.  derive_slots passes no slot mapping (the
-    library derives the slots from the block table).  Returns (out, lse) as
-    CPU tensors."""
+    library derives the slots from the block table).  inline_desc passes
+    the descriptor as host copies only (no device cu_seqlens_q,
+    cached_seq_len or block_table).  attention_twice runs the attention
+    launch a second time on the same prepared workspace and checks that it
+    reproduces the first output bit for bit.  Returns (out, lse) as CPU
+    tensors."""
     qd = q.to(DEV) if q is not None else None
     kd, vd = k_new.to(DEV), v_new.to(DEV)
     out = torch.empty_like(qd) if qd is not None else None
     lse = None
     if want_lse and qd is not None:
         lse = torch.full((qd.shape[1], qd.shape[0]), float("nan"), dtype=torch.float32, device=DEV)
-    call = AttnCall(q=qd, k_new=kd, v_new=vd, k_cache=cache.k, v_cache=cache.v, out=out,
-                    cu_seqlens_q=_dev(batch["cu_seqlens_q"], np.int32),
+    if inline_desc:
+        desc = dict(cu_seqlens_q=None, cached_seq_len=None, block_table=None,
+                    h_block_table=np.asarray(batch["block_table"], np.int32))
+    else:
+        desc = dict(cu_seqlens_q=_dev(batch["cu_seqlens_q"], np.int32),
                     cached_seq_len=_dev(batch["cached_seq_len"], np.int32),
-                    block_table=_dev(batch["block_table"], np.int32),
+                    block_table=_dev(batch["block_table"], np.int32))
+    call = AttnCall(q=qd, k_new=kd, v_new=vd, k_cache=cache.k, v_cache=cache.v, out=out, **desc,
                     slot_mapping=None if derive_slots else _dev(batch["slot_mapping"], np.int64),
                     h_cu_seqlens_q=batch["cu_seqlens_q"], h_cached_seq_len=batch["cached_seq_len"],
                     kv_segment_size=kv_segment_size, scale=scale, lse=lse,
@@ -111,6 +120,13 @@ def gpu_call(cache, batch, q, k_new, v_new, kv_segment_size, *, scale=None, want
     call.set_workspace(ws)
     call()
     torch.cuda.synchronize()
+    if attention_twice and out is not None:
+        first = out.clone()
+        out.fill_(float("nan"))
+        call.attention()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                           first.view(torch.int16) if first.dtype == torch.bfloat16 else first)
     return (out.cpu() if out is not None else None), (lse.cpu() if lse is not None else None)
 
 

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(lib, name), f"{name} declared but not exported"
     assert set(declared) == set(_lib.SIGNATURES), "binding and header disagree"
-    assert lib.cpa_abi_version() == 2
+    assert lib.cpa_abi_version() == 3
 
 
 def test_status_strings():
@@ -156,3 +156,43 @@ def test_bad_rope_requests_are_refused(rope, over):
     assert _lib.lib().cpa_rope_reshape_and_cache(ctypes.byref(a), p, None) == _lib.CPA_ERR_INVALID_ARG
     assert _lib.lib().cpa_rope_prepare(ctypes.byref(a), p, None) == _lib.CPA_ERR_INVALID_ARG
     assert _lib.lib().cpa_rope_chunked_prefill_attn(ctypes.byref(a), p, None) == _lib.CPA_ERR_INVALID_ARG
+
+
+def test_binding_struct_matches_the_header(tmp_path):
+    """Size and field offsets of cpa_attn_args as the C compiler lays it out
+    against the binding's ctypes mirror, and the inline-descriptor limit."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    fields = [f for f, _ in _lib.AttnArgs._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"chunked_prefill_attn.h\"\n"
+                   "int main(void) {\n  printf(\"%zu %d\\n\", sizeof(cpa_attn_args), CPA_INLINE_DESC_INTS);\n"
+                   + "".join('  printf("%%zu\\n", offsetof(cpa_attn_args, %s));\n' % f for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    assert int(out[0]) == ctypes.sizeof(_lib.AttnArgs)
+    assert int(out[1]) == _lib.CPA_INLINE_DESC_INTS
+    for f, off in zip(fields, out[2:]):
+        assert int(off) == getattr(_lib.AttnArgs, f).offset, f
+
+
+def test_inline_descriptor_replaces_the_device_arrays():
+    """With host copies of the whole descriptor the device arrays may be
+    absent; past the inline limit they are required again."""
+    lib = _lib.lib()
+    bt = np.zeros((2, 200), dtype=np.int32)
+    a, _keep = _args(cu_seqlens_q=None, cached_seq_len=None, block_table=None)
+    assert lib.cpa_check_args(ctypes.byref(a)) == _lib.CPA_ERR_INVALID_ARG
+    a.h_block_table = bt.ctypes.data                      # 2*2 + 1 + 400 ints: inline
+    assert lib.cpa_check_args(ctypes.byref(a)) == _lib.CPA_OK
+    big = np.zeros((2, 500), dtype=np.int32)              # 1005 ints: too many
+    a.max_blocks_per_seq, a.h_block_table = 500, big.ctypes.data
+    assert 2 * 2 + 1 + 2 * 500 > _lib.CPA_INLINE_DESC_INTS
+    assert lib.cpa_check_args(ctypes.byref(a)) == _lib.CPA_ERR_INVALID_ARG
+    a.cu_seqlens_q = a.cached_seq_len = a.block_table = 0x1000
+    assert lib.cpa_check_args(ctypes.byref(a)) == _lib.CPA_OK

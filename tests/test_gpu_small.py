@@ -38,7 +38,7 @@ def _resolve(v, S):
     return {"S": S, "2S": 2 * S}.get(v, v)
 
 
-def run_case(case, split, fill=0.0, seed=0, derive_slots=False):
+def run_case(case, split, fill=0.0, seed=0, derive_slots=False, inline_desc=False):
     name, dtype, H, G, D, bs, S, reqs, decodes, budget = case
     rng = np.random.default_rng(1000 + seed)
     max_blocks = max(-(-(p + 1) // bs) for p, _ in reqs + [(c + 1, 0) for c in decodes]) + 1
@@ -70,7 +70,7 @@ def run_case(case, split, fill=0.0, seed=0, derive_slots=False):
     sp, sd = (_resolve(x, S) for x in SPLITS[split])
     say(f"case {name} split={split} T={T} seqs={pb['num_seqs']}")
     out, _ = gpu_call(pair.cache, pb, qt, kt, vt, S, split_pre=sp, split_dec=sd,
-                      derive_slots=derive_slots)
+                      derive_slots=derive_slots, inline_desc=inline_desc, attention_twice=inline_desc)
     ref = pair.oracle_batch(ob, q64, k64, v64, 1 / math.sqrt(D), G)
     return pair, out, ref, dtype
 
@@ -95,6 +95,22 @@ def test_slots_derived_from_the_block_table(case):
     need_gpu()
     pair, out, ref, dtype = run_case(case, "auto", derive_slots=True)
     assert_close(out.to(torch.float64).numpy(), ref, dtype, f"{case[0]}/derived slots")
+    gk, gv = pair.cache.canonical_bits()
+    assert np.array_equal(gk, bits_of(pair.k_pool, dtype))
+    assert np.array_equal(gv, bits_of(pair.v_pool, dtype))
+
+
+@pytest.mark.parametrize("split", ["auto", "seg2"])
+@pytest.mark.parametrize("case", [CASES[1], CASES[6], CASES[8], CASES[9], CASES[10]],
+                         ids=["ragged", "fp32", "tiny", "hpg3_bs64", "hpg6_bs256"])
+def test_inline_descriptor_matches_oracle(case, split):
+    """The descriptor passed as host copies only (kernel arguments of the
+    prepare launch, a workspace copy for the attention launch), with slots
+    derived from the block table; the attention launch run twice on the one
+    prepared workspace gives the same bits."""
+    need_gpu()
+    pair, out, ref, dtype = run_case(case, split, derive_slots=True, inline_desc=True)
+    assert_close(out.to(torch.float64).numpy(), ref, dtype, f"{case[0]}/{split}/inline")
     gk, gv = pair.cache.canonical_bits()
     assert np.array_equal(gk, bits_of(pair.k_pool, dtype))
     assert np.array_equal(gv, bits_of(pair.v_pool, dtype))

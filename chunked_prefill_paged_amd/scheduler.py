@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import ctypes
+import weakref
 
 import numpy as np
 
@@ -57,12 +58,9 @@ class HostScheduler:
                    "cpa_sched_create")
         self._h = handle
         self._max_seqs = 0
-
-    def __del__(self):
-        h = getattr(self, "_h", None)
-        if h:
-            _lib.lib().cpa_sched_destroy(h)
-            self._h = None
+        # released when the object is collected or, at the latest, at
+        # interpreter exit while the library is still loaded
+        self._release = weakref.finalize(self, _lib.lib().cpa_sched_destroy, handle)
 
     def add_request(self, req_id: int, num_prompt_tokens: int, prefix_blocks=()):
         blocks = np.ascontiguousarray(prefix_blocks, dtype=np.int32)

@@ -56,6 +56,9 @@ def _args():
     ap.add_argument("--split-keys-prefill", type=int, default=0,
                     help="0 automatic, -1 never, else keys per work item")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-timing", choices=("dispatch", "records"), default="dispatch",
+                    help="per-launch attention timing: events taken by the kernel's own dispatch "
+                         "(cpa_attention_timed), or event records around the launch")
     ap.add_argument("--workload", choices=("c2", "c4", "c5", "rope"), default="c2",
                     help="c2: the 10k prompt (headline line); c5: the 32k prompt, per chunk "
                          "and against one monolithic call; c4: the mixed decode + prefill batch; "
@@ -224,14 +227,45 @@ class PromptBench:
             call.args.h_cached_seq_len = b["cached_seq_len"].ctypes.data
             call._keep_host = (b["cu_seqlens_q"], b["cached_seq_len"], bt)
             call.prepare()
-            if events is not None:
+            if events is None:
+                call.attention()
+            elif isinstance(events[i][0], int):        # raw events taken by the dispatch
+                call.attention_timed(events[i][0], events[i][1])
+            else:                                      # event records around the launch
                 events[i][0].record()
-            call.attention()
-            if events is not None:
+                call.attention()
                 events[i][1].record()
             sched.commit()
         sched.free_request(self.rid)
         self.rid += 1
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime the process already uses
+    (torch's), for launches that take their timing events in the dispatch."""
+
+    def __init__(self):
+        import ctypes
+        self._c = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+
+    def _check(self, err, what):
+        if err != 0:
+            raise RuntimeError(f"{what} failed ({err})")
+
+    def create(self) -> int:
+        ev = self._c.c_void_p()
+        self._check(self.hip.hipEventCreate(self._c.byref(ev)), "hipEventCreate")
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = self._c.c_float()
+        self._check(self.hip.hipEventElapsedTime(self._c.byref(ms), self._c.c_void_p(a),
+                                                 self._c.c_void_p(b)), "hipEventElapsedTime")
+        return ms.value
+
+    def destroy(self, ev: int) -> None:
+        self._check(self.hip.hipEventDestroy(self._c.c_void_p(ev)), "hipEventDestroy")
 
 
 def cpu_baseline(w, max_blocks):
@@ -549,8 +583,14 @@ def main():
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
-    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in bench.chunks] for _ in range(args.steps)]
+    if args.event_timing == "dispatch":
+        hip = HipEvents()
+        events = [[(hip.create(), hip.create()) for _ in bench.chunks] for _ in range(args.steps)]
+        elapsed_ms = hip.elapsed_ms
+    else:
+        events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in bench.chunks] for _ in range(args.steps)]
+        elapsed_ms = lambda a, b: a.elapsed_time(b)   # noqa: E731
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -558,9 +598,14 @@ def main():
         bench.step(ev)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    attn_ms = sum(a.elapsed_time(b) for step in events for (a, b) in step)
-    per_chunk_ms = [sum(events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps))
+    attn_ms = sum(elapsed_ms(a, b) for step in events for (a, b) in step)
+    per_chunk_ms = [sum(elapsed_ms(*events[s][i]) for s in range(args.steps))
                     / args.steps for i in range(len(bench.chunks))]
+    if args.event_timing == "dispatch":
+        for step in events:
+            for a, b in step:
+                hip.destroy(a)
+                hip.destroy(b)
     value = flops * args.steps / elapsed / 1e12
     achieved = flops * args.steps / (attn_ms / 1e3) / 1e12
     w = bench.w
@@ -589,7 +634,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic() if args.kv_cache == "bf16" else None,
-                     "kernel": "attn_kernel<bf16,128> (+ merge_kernel when rows are split)"},
+                     "kernel": "attn_kernel<bf16,128> (+ merge_kernel when rows are split)",
+                     "timing": ("HIP events taken by the attention kernel's dispatch "
+                                "(hipExtLaunchKernel), every launch of the timed steps"
+                                if args.event_timing == "dispatch" else
+                                "HIP event records around every attention launch of the timed steps")},
         "plan": [{"items": p["num_items"], "merge_rows": p["num_merge_rows"]} for p in bench.plan],
     }
     if not args.no_cpu_baseline and args.kv_cache == "bf16":

@@ -83,6 +83,7 @@ SIGNATURES = {
     "cpa_reshape_and_cache": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _vp]),
     "cpa_prepare": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _vp]),
     "cpa_attention": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _vp]),
+    "cpa_attention_timed": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _vp, _vp, _vp]),
     "cpa_chunked_prefill_attn": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _vp]),
     "cpa_rope_reshape_and_cache": (ctypes.c_int, [ctypes.POINTER(AttnArgs), ctypes.POINTER(RopeArgs), _vp]),
     "cpa_rope_prepare": (ctypes.c_int, [ctypes.POINTER(AttnArgs), ctypes.POINTER(RopeArgs), _vp]),

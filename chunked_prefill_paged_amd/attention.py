@@ -151,6 +151,12 @@ class AttnCall:
         _lib.check(_lib.lib().cpa_attention(ctypes.byref(self.args), _stream(stream)),
                    "cpa_attention")
 
+    def attention_timed(self, start_event, stop_event, stream=None) -> None:
+        """attention() with the kernel's dispatch taking two raw hipEvent_t
+        handles (ints): their elapsed time is the kernel's duration."""
+        _lib.check(_lib.lib().cpa_attention_timed(ctypes.byref(self.args), _stream(stream),
+                                                  start_event, stop_event), "cpa_attention_timed")
+
     def __call__(self, stream=None) -> None:
         _lib.check(_lib.lib().cpa_chunked_prefill_attn(ctypes.byref(self.args), _stream(stream)),
                    "cpa_chunked_prefill_attn")

@@ -38,6 +38,7 @@
 //     contiguous range of (KV head, item) pairs: one KV head per XCD L2 when
 //     G = 8.  Items are ordered longest-first within a sequence.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -1635,7 +1636,8 @@ cpa_status launch_prep(const cpa_attn_args* a, const Resolved* r, bool plan, con
 }
 
 template <typename T, int D, bool FP8>
-cpa_status launch_attention(const cpa_attn_args* a, const Resolved* r, hipStream_t stream) {
+cpa_status launch_attention(const cpa_attn_args* a, const Resolved* r, hipStream_t stream,
+                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
     char* ws = (char*)a->workspace;
     if (r->items > 0) {
         AttnParams p{};
@@ -1672,7 +1674,11 @@ cpa_status launch_attention(const cpa_attn_args* a, const Resolved* r, hipStream
         p.scale_log2 = a->scale * 1.44269504088896340736f * (FP8 ? scale_or_one(a->k_scale) : 1.f);
         p.v_scale = FP8 ? scale_or_one(a->v_scale) : 1.f;
         const int grid = (int)(r->items * a->num_kv_heads);
-        hipLaunchKernelGGL((attn_kernel<T, D, FP8>), dim3(grid), dim3(kThreads), 0, stream, p);
+        if (ev0 || ev1)   // events taken by the dispatch itself
+            hipExtLaunchKernelGGL((attn_kernel<T, D, FP8>), dim3(grid), dim3(kThreads), 0, stream, ev0, ev1, 0,
+                                  p);
+        else
+            hipLaunchKernelGGL((attn_kernel<T, D, FP8>), dim3(grid), dim3(kThreads), 0, stream, p);
         if (hipGetLastError() != hipSuccess) return CPA_ERR_HIP;
     }
     if (r->merge > 0) {
@@ -1726,15 +1732,16 @@ cpa_status check_rope(const cpa_attn_args* a, const cpa_rope_args* rope) {
     return CPA_OK;
 }
 
-cpa_status attn_dispatch(const cpa_attn_args* a, const Resolved* r, hipStream_t s) {
+cpa_status attn_dispatch(const cpa_attn_args* a, const Resolved* r, hipStream_t s, hipEvent_t e0 = nullptr,
+                         hipEvent_t e1 = nullptr) {
     if (kv_fp8(a))
-        return a->head_dim == 128 ? launch_attention<__bf16, 128, true>(a, r, s)
-                                  : launch_attention<__bf16, 64, true>(a, r, s);
+        return a->head_dim == 128 ? launch_attention<__bf16, 128, true>(a, r, s, e0, e1)
+                                  : launch_attention<__bf16, 64, true>(a, r, s, e0, e1);
     if (a->dtype == CPA_BF16)
-        return a->head_dim == 128 ? launch_attention<__bf16, 128, false>(a, r, s)
-                                  : launch_attention<__bf16, 64, false>(a, r, s);
+        return a->head_dim == 128 ? launch_attention<__bf16, 128, false>(a, r, s, e0, e1)
+                                  : launch_attention<__bf16, 64, false>(a, r, s, e0, e1);
     if (a->head_dim == 128) return CPA_ERR_UNSUPPORTED;   // fp32 D=128 needs 128 KiB of LDS tiles
-    return launch_attention<float, 64, false>(a, r, s);
+    return launch_attention<float, 64, false>(a, r, s, e0, e1);
 }
 
 cpa_status check_workspace(const cpa_attn_args* a, const Resolved* r) {
@@ -1818,6 +1825,16 @@ cpa_status cpa_attention(const cpa_attn_args* a, void* stream) {
     if ((st = check_pointers(a, true)) != CPA_OK) return st;
     if ((st = check_workspace(a, &r)) != CPA_OK) return st;
     return attn_dispatch(a, &r, (hipStream_t)stream);
+}
+
+cpa_status cpa_attention_timed(const cpa_attn_args* a, void* stream, void* start_event, void* stop_event) {
+    if (!start_event || !stop_event) return CPA_ERR_INVALID_ARG;
+    Resolved r;
+    cpa_status st = resolve(a, &r);
+    if (st != CPA_OK) return st;
+    if ((st = check_pointers(a, true)) != CPA_OK) return st;
+    if ((st = check_workspace(a, &r)) != CPA_OK) return st;
+    return attn_dispatch(a, &r, (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event);
 }
 
 cpa_status cpa_chunked_prefill_attn(const cpa_attn_args* a, void* stream) {

@@ -188,6 +188,16 @@ cpa_status cpa_prepare(const cpa_attn_args* args, void* stream);
  * (e.g. once per layer with other q/cache/out pointers of the same shapes). */
 cpa_status cpa_attention(const cpa_attn_args* args, void* stream);
 
+/* cpa_attention with the attention kernel's own dispatch taking two events
+ * (hipEvent_t, created by the caller on the device of `stream`): start_event
+ * when the kernel starts, stop_event when it ends, so that their elapsed
+ * time is the kernel's duration with no event records of their own in the
+ * stream.  The merge launch of split rows, if any, follows stop_event.  For
+ * callers that time the kernel inside a measured loop.  CPA_ERR_INVALID_ARG
+ * for a NULL event; otherwise as cpa_attention. */
+cpa_status cpa_attention_timed(const cpa_attn_args* args, void* stream, void* start_event,
+                               void* stop_event);
+
 /* cpa_prepare followed by cpa_attention: the whole chunk step. */
 cpa_status cpa_chunked_prefill_attn(const cpa_attn_args* args, void* stream);
 

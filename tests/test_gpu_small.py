@@ -6,6 +6,8 @@ import numpy as np
 import pytest
 import torch
 
+from chunked_prefill_paged_amd import AttnCall
+
 from tests.gpu_helpers import (DEV, Pair, assert_close, bits_of, gpu_call, need_gpu, quantize,
                                say)
 
@@ -204,6 +206,42 @@ def test_growing_scores_move_the_reference(split):
     out, _ = gpu_call(pair.cache, pb, qt, kt[computed:], vt[computed:], S, split_pre=split)
     ref = pair.oracle_batch(ob, q64, k64[computed:], v64[computed:], 1 / math.sqrt(D), G)
     assert_close(out.to(torch.float64).numpy(), ref, "bf16", f"growing/{split}")
+
+
+def test_timed_attention_matches_and_times_the_kernel():
+    """cpa_attention_timed: the same output bits as cpa_attention, and a
+    positive elapsed time between the two events its dispatch takes."""
+    need_gpu()
+    import bench
+    H, G, D, bs, S = 32, 8, 128, 16, 512
+    rng = np.random.default_rng(5)
+    pair = Pair(200, G, bs, D, "bf16", 4096, 120, rng.permutation(200).astype(np.int32))
+    pair.add_partial(0, 1500, 1000)
+    kt, k64 = quantize(rng.standard_normal((1000, G, D)), "bf16")
+    vt, v64 = quantize(rng.standard_normal((1000, G, D)), "bf16")
+    pair.fill_context(0, k64, v64, kt, vt)
+    pb, ob = pair.step()
+    qt, _ = quantize(rng.standard_normal((500, H, D)), "bf16")
+    kn, _ = quantize(rng.standard_normal((500, G, D)), "bf16")
+    vn, _ = quantize(rng.standard_normal((500, G, D)), "bf16")
+    out, _ = gpu_call(pair.cache, pb, qt, kn, vn, S)
+    q, k, v = qt.to(DEV), kn.to(DEV), vn.to(DEV)
+    out2 = torch.full_like(q, float("nan"))
+    call = AttnCall(q=q, k_new=k, v_new=v, k_cache=pair.cache.k, v_cache=pair.cache.v, out=out2,
+                    cu_seqlens_q=None, cached_seq_len=None, block_table=None, slot_mapping=None,
+                    h_cu_seqlens_q=pb["cu_seqlens_q"], h_cached_seq_len=pb["cached_seq_len"],
+                    h_block_table=pb["block_table"], kv_segment_size=S)
+    call.set_workspace(torch.empty(call.workspace_bytes(), dtype=torch.uint8, device=DEV))
+    hip = bench.HipEvents()
+    e0, e1 = hip.create(), hip.create()
+    call.prepare()
+    call.attention_timed(e0, e1)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(e0, e1)
+    hip.destroy(e0)
+    hip.destroy(e1)
+    assert ms > 0.0
+    assert torch.equal(out2.cpu().view(torch.int16), out.view(torch.int16))
 
 
 def test_empty_sequence_in_batch_and_lse():

@@ -46,12 +46,16 @@ def _dev(a, dt):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(DEV)
 
 
-def _call(cache, batch, qd, kd, vd, S, derive_slots, out=None):
-    return AttnCall(q=qd, k_new=kd, v_new=vd, k_cache=cache.k, v_cache=cache.v,
-                    out=out if out is not None else torch.empty_like(qd),
-                    cu_seqlens_q=_dev(batch["cu_seqlens_q"], np.int32),
+def _call(cache, batch, qd, kd, vd, S, derive_slots, out=None, inline_desc=False):
+    if inline_desc:      # host copies only: the descriptor rides in the launch arguments
+        desc = dict(cu_seqlens_q=None, cached_seq_len=None, block_table=None,
+                    h_block_table=np.asarray(batch["block_table"], np.int32))
+    else:
+        desc = dict(cu_seqlens_q=_dev(batch["cu_seqlens_q"], np.int32),
                     cached_seq_len=_dev(batch["cached_seq_len"], np.int32),
-                    block_table=_dev(batch["block_table"], np.int32),
+                    block_table=_dev(batch["block_table"], np.int32))
+    return AttnCall(q=qd, k_new=kd, v_new=vd, k_cache=cache.k, v_cache=cache.v,
+                    out=out if out is not None else torch.empty_like(qd), **desc,
                     slot_mapping=None if derive_slots else _dev(batch["slot_mapping"], np.int64),
                     h_cu_seqlens_q=batch["cu_seqlens_q"], h_cached_seq_len=batch["cached_seq_len"],
                     kv_segment_size=S)
@@ -116,9 +120,12 @@ def test_rotated_queries_and_cache_match_oracle(case, interleaved, derive_slots)
     assert torch.equal(qd.cpu(), qt)
 
 
-@pytest.mark.parametrize("case", [CASES[1], CASES[2], CASES[4], CASES[5]],
-                         ids=[CASES[i][0] for i in (1, 2, 4, 5)])
-def test_rotary_chunk_step_matches_oracle_attention(case):
+_STEP = [(1, False), (2, False), (4, False), (5, False), (1, True), (2, True), (4, True)]
+
+
+@pytest.mark.parametrize("case,inline_desc", [(CASES[i], il) for i, il in _STEP],
+                         ids=[CASES[i][0] + ("/inline" if il else "") for i, il in _STEP])
+def test_rotary_chunk_step_matches_oracle_attention(case, inline_desc):
     need_gpu()
     name, dtype, H, G, D, bs, S = case[:7]
     theta = 10000.0
@@ -127,7 +134,8 @@ def test_rotary_chunk_step_matches_oracle_attention(case):
     qd = qt.to(DEV)
     q_out = torch.empty_like(qd)
     out = torch.full_like(qd, float("nan"))
-    call = _call(pair.cache, pb, qd, kt.to(DEV), vt.to(DEV), S, derive_slots=True, out=out)
+    call = _call(pair.cache, pb, qd, kt.to(DEV), vt.to(DEV), S, derive_slots=True, out=out,
+                 inline_desc=inline_desc)
     ws = torch.empty(max(256, call.workspace_bytes()), dtype=torch.uint8, device=DEV)
     call.set_workspace(ws)
     call.rope_call(Rope(q_out, theta))

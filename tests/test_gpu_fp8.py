@@ -50,11 +50,15 @@ class Fp8Pools:
         return (self.k.permute(0, 2, 1, 3).contiguous().cpu().numpy(),
                 self.v.permute(0, 3, 1, 2).contiguous().cpu().numpy())
 
-    def call(self, batch, q, k, v, S, ks, vs, out=None, slots=True, **kw):
-        return AttnCall(q=q, k_new=k, v_new=v, k_cache=self.k, v_cache=self.v, out=out,
-                        cu_seqlens_q=_dev(batch["cu_seqlens_q"], np.int32),
+    def call(self, batch, q, k, v, S, ks, vs, out=None, slots=True, inline_desc=False, **kw):
+        if inline_desc:   # host copies only: the descriptor rides in the launch arguments
+            desc = dict(cu_seqlens_q=None, cached_seq_len=None, block_table=None,
+                        h_block_table=np.asarray(batch["block_table"], np.int32))
+        else:
+            desc = dict(cu_seqlens_q=_dev(batch["cu_seqlens_q"], np.int32),
                         cached_seq_len=_dev(batch["cached_seq_len"], np.int32),
-                        block_table=_dev(batch["block_table"], np.int32),
+                        block_table=_dev(batch["block_table"], np.int32))
+        return AttnCall(q=q, k_new=k, v_new=v, k_cache=self.k, v_cache=self.v, out=out, **desc,
                         slot_mapping=_dev(batch["slot_mapping"], np.int64) if slots else None,
                         h_cu_seqlens_q=batch["cu_seqlens_q"], h_cached_seq_len=batch["cached_seq_len"],
                         kv_segment_size=S, k_scale=ks, v_scale=vs, **kw)
@@ -64,7 +68,7 @@ class Fp8Pools:
                                            ks, vs)
 
 
-def _run(case, split, derive_slots=False, seed=0):
+def _run(case, split, derive_slots=False, seed=0, inline_desc=False):
     name, H, G, D, bs, S, reqs, decodes, budget, ks, vs = case
     rng = np.random.default_rng(7000 + seed)
     max_blocks = max(-(-(p + 1) // bs) for p, _ in reqs + [(c + 1, 0) for c in decodes]) + 1
@@ -103,7 +107,7 @@ def _run(case, split, derive_slots=False, seed=0):
     qd = qt.to(DEV)
     out = torch.full_like(qd, float("nan"))
     call = pools.call(pb, qd, kt.to(DEV), vt.to(DEV), S, ks, vs, out=out, slots=not derive_slots,
-                      split_keys_prefill=sp, split_keys_decode=sd)
+                      inline_desc=inline_desc, split_keys_prefill=sp, split_keys_decode=sd)
     call.set_workspace(torch.empty(max(256, call.workspace_bytes()), dtype=torch.uint8, device=DEV))
     call()
     torch.cuda.synchronize()
@@ -123,6 +127,18 @@ def test_fp8_cache_attention_matches_oracle(case, split):
     assert np.array_equal(gk, pools.ok), "K codes differ"
     assert np.array_equal(gv, pools.ov), "V codes differ"
     assert_close(out.to(torch.float64).cpu().numpy(), ref, "bf16", f"fp8 {case[0]}/{split}")
+
+
+@pytest.mark.parametrize("case", [CASES[1], CASES[3], CASES[5]],
+                         ids=[CASES[1][0], CASES[3][0], CASES[5][0]])
+def test_fp8_cache_with_inline_descriptor(case):
+    """The fp8 cache write and attention with the descriptor given as host
+    copies only, slots derived from the block table."""
+    need_gpu()
+    pools, out, ref = _run(case, "seg", derive_slots=True, seed=2, inline_desc=True)
+    gk, gv = pools.canonical()
+    assert np.array_equal(gk, pools.ok) and np.array_equal(gv, pools.ov)
+    assert_close(out.to(torch.float64).cpu().numpy(), ref, "bf16", f"fp8 inline {case[0]}")
 
 
 @pytest.mark.parametrize("case", [CASES[1], CASES[4]], ids=[CASES[1][0], CASES[4][0]])

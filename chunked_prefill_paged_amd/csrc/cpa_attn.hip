@@ -568,18 +568,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     // the sequence end first mask their scores to -inf).  LDS fragments are prefetched three MFMAs ahead through four
     // rotating registers; sched_barrier fences pin the order:
     //   P1  S0 = K[0:32] Q^T - m2   (8 MFMAs)
-    //   P2  S1 = K[32:64] Q^T - m2  (8 MFMAs)  || exp, sum, convert of S0
-    //   P3  O += V[0:32] P0         (8 MFMAs)  || exps of S1's keys 32..47
-    //   P4  O += V[32:64] P1        (8 MFMAs)  || exps of keys 48..63 (under the PV of keys
-    //                                              32..47), then the next tile's -m2 presets
-    // The reference maximum of a row moves only when the exps of some lane's
-    // share of a block (16 keys of S0, 8 keys of either half of S1) sum past
-    // 2^12 (2^11 for 8 keys), so that one of them exceeds 2^8: the common
-    // path takes no maximum and needs no exchange between the two lanes of a
-    // row, and keeps every exp2 argument <= 12; the rare path takes the row
-    // maximum, raises the reference to it and rescales O and l.  Each share
-    // is checked before its PV is issued and after every PV formed under the
-    // old reference, so a rescale covers exactly those products.
+    //   P2  S1 = K[32:64] Q^T - m2  (8 MFMAs)  || exp, sum, convert of S0, then S0's check
+    //   P3  O += V[0:32] P0         (8 MFMAs)  || exp, sum, convert of S1, then S1's check
+    //   P4  O += V[32:64] P1        (8 MFMAs)  || the next tile's -m2 presets
+    // The reference maximum of a row moves only when the 16 exps of some
+    // lane's share of a 32-key block sum past 2^12, so that one of them
+    // exceeds 2^8: the common path takes no maximum and needs no exchange
+    // between the two lanes of a row, and keeps every exp2 argument <= 12;
+    // the rare path takes the row maximum, raises the reference to it and
+    // rescales O and l.  Each block is checked before its PV is issued and
+    // after every PV formed under the old reference, so a rescale covers
+    // exactly those products.
     constexpr bool kHandOrdered = (KPL == 8 && D == 128);
     // LDS byte offsets of this lane's fragments: K fragment (k-step s8,
     // 32-key block sb) at k_base + ((s8*16) ^ k_x) + sb*32*D*2; V fragment
@@ -715,71 +714,46 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             rs = 0.f;
             if (masked) apply_mask(S1, 1);
             __builtin_amdgcn_sched_barrier(0);
-            // P3: PV of the first half; exps of S1's registers 0..7
+            // P3: PV of the first half under the exps of S1
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 fr[(i + 3) & 3] = frag(16 + i + 3);
                 oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
-                if (i < 4) ex2(S1, 2, 2 * i);
+                ex2(S1, 2 + (i >> 2), 2 * i);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (over(rs, 2048.f)) {
+            if (over(rs, 4096.f)) {
                 const float sh = decide(tmax(S1, 0));
                 rs = 0.f;
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     S1[r] -= sh;
                     S1[r + 1] -= sh;
-                    if (r < 8) ex2(S1, 2, r);
+                    ex2(S1, 2 + (r >> 3), r);
                 }
             }
-            l_run += rs;                 // before the second decision may rescale l
-            rs = 0.f;
+            l_run += rs;
             __builtin_amdgcn_sched_barrier(0);
-            // P4: PV of keys 32..47 under the exp of registers 8..15, then
-            // (after their own check) PV of keys 48..63
-#pragma unroll
-            for (int i = 8; i < 12; ++i) {
-                fr[(i + 3) & 3] = frag(16 + i + 3);
-                oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
-                ex2(S1, 3, 8 + 2 * (i - 8));
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (over(rs, 2048.f)) {
-                const float sh = decide(tmax(S1, 8));
-                rs = 0.f;
-#pragma unroll
-                for (int r = 8; r < 16; r += 2) {
-                    S1[r] -= sh;
-                    S1[r + 1] -= sh;
-                    ex2(S1, 3, r);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // the reference is final for this tile: preset the next tile's
-            // accumulators under the last PV
-            // (as pairs: one 64-bit move sets two registers)
+            // P4: PV of the second half; the reference is final for this
+            // tile, so the next tile's accumulators are preset under it (as
+            // pairs: one 64-bit move sets two registers)
             typedef uint64_t u64x8 __attribute__((ext_vector_type(8)));
             const uint64_t nb = __builtin_bit_cast(uint32_t, ref_nm());
             const uint64_t n2 = (nb << 32) | nb;
             u64x8 z0 = __builtin_bit_cast(u64x8, S0), z1 = __builtin_bit_cast(u64x8, S1);
 #pragma unroll
-            for (int i = 12; i < 16; ++i) {
+            for (int i = 8; i < 16; ++i) {
                 if (i + 3 < 16) fr[(i + 3) & 3] = frag(16 + i + 3);
                 oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
-#pragma unroll
-                for (int j = 2 * (i - 12); j < 2 * (i - 11); ++j) {
-                    uint64_t x0, x1;
-                    asm volatile("v_mov_b64 %0, %1" : "=v"(x0) : "v"(n2));
-                    asm volatile("v_mov_b64 %0, %1" : "=v"(x1) : "v"(n2));
-                    z0[j] = x0;
-                    z1[j] = x1;
-                }
+                uint64_t x0, x1;
+                asm volatile("v_mov_b64 %0, %1" : "=v"(x0) : "v"(n2));
+                asm volatile("v_mov_b64 %0, %1" : "=v"(x1) : "v"(n2));
+                z0[i - 8] = x0;
+                z1[i - 8] = x1;
                 __builtin_amdgcn_sched_barrier(0);
             }
             S0 = __builtin_bit_cast(f32x16, z0);
             S1 = __builtin_bit_cast(f32x16, z1);
-            l_run += rs;
         }
     };
 

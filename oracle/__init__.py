@@ -21,7 +21,8 @@ Everything is written as the plain definition, in float64, from these pages:
   allocation (section 2.1), block-aligned budget (section 2.3).
 
 ``prefix_cache`` and the prefix-caching part of ``schedule`` follow the
-block hash chain, full-block matching and the pool's three buckets
+parent-chained block identity (kept exact: a trie of token blocks instead
+of a digest), full-block matching and the pool's three buckets
 ("Prefill Optimisation ...", sections 3 and 7) and the first-chunk-only
 lookup ("vLLM Chunked Prefill ...", sections 2.2 and 3.1).
 

@@ -1,72 +1,83 @@
-"""Oracle for prefix-cache block identity: the parent-chained block hash and
-full-block prefix matching.
+"""Oracle for prefix-cache block identity and full-block prefix matching.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-"Prefill Optimisation: Prefix Caching, Chunked Prefill, and
-Disaggregation", section 3 ("vLLM block hash chain") and section 7 (the
-pedagogical prefix cache):
-* the cache is keyed per full block; a block's digest covers its parent
-  block's digest, the scope (namespace) and the block's ordered token ids,
-  so a change anywhere earlier changes every later digest;
-* only full blocks are hashed and reused (tokens in multiples of the block
-  size);
-* matching walks the chain from the first block and stops at the first
-  block whose digest is unknown.
+What the pages fix ("Prefill Optimisation: Prefix Caching, Chunked Prefill,
+and Disaggregation", section 3, "vLLM block hash chain", and the behaviour
+its section 7 script prints):
+* reuse is per full block; a partial last block is never shared;
+* a block is the same block only if its own ordered token ids, its scope
+  (a namespace that keeps tenants or models apart) and everything before it
+  are the same, so one changed token changes the identity of its block and
+  of every later block;
+* a lookup walks the prompt's full blocks from the first and stops at the
+  first block that is not known.
 
-The digest here follows the section 7 construction: SHA-256 over the
-parent digest (hex text, "ROOT" for the first block) and the namespace, both
-as UTF-8, then every token id as 4 unsigned big-endian bytes.
+The pages build that identity with a cryptographic digest chained through
+the parent's digest.  Here it is exact instead: every full block is a node
+of one trie, reached from its scope's root by the token tuples of the
+blocks before it, and its identity is the node's integer id.  Two blocks
+share an identity exactly when scope and all tokens up to the block's end
+agree, so no collision question arises.  Identities are only compared with
+each other inside one process; the product's own digests are never
+compared with them.
 """
 from __future__ import annotations
 
-import hashlib
-
-ROOT = "ROOT"
-
-
-def block_hash(parent: str, block_tokens, namespace: str) -> str:
-    """Hex digest of one full block given its parent's digest."""
-    h = hashlib.sha256()
-    h.update(parent.encode("utf-8"))
-    h.update(namespace.encode("utf-8"))
-    for tok in block_tokens:
-        h.update(int(tok).to_bytes(4, byteorder="big", signed=False))
-    return h.hexdigest()
+# (parent node id, block token tuple) -> node id; a scope's root is keyed
+# (-1, ("scope", name)).  The registry only grows; ids are process-local.
+_nodes: dict = {}
 
 
-def chain(tokens, block_size: int, namespace: str) -> list:
-    """Digests of the full blocks of ``tokens``, in order."""
-    out, parent = [], ROOT
-    for i in range(len(tokens) // block_size):
-        parent = block_hash(parent, tokens[i * block_size:(i + 1) * block_size], namespace)
-        out.append(parent)
-    return out
+def _intern(key) -> int:
+    node = _nodes.get(key)
+    if node is None:
+        node = len(_nodes)
+        _nodes[key] = node
+    return node
 
 
-class PrefixCache:
-    """Set of known block digests (no pool): what ``match_prefix`` can reuse."""
+def scope_root(scope: str) -> int:
+    """Identity of the empty prefix under ``scope``."""
+    return _intern((-1, ("scope", str(scope))))
+
+
+def next_identity(parent: int, block_tokens) -> int:
+    """Identity of the full block ``block_tokens`` that follows ``parent``."""
+    return _intern((int(parent), tuple(int(t) for t in block_tokens)))
+
+
+def prefix_identities(tokens, block_size: int, scope: str) -> list:
+    """Identities of the full blocks of ``tokens``, first block first."""
+    ids = []
+    node = scope_root(scope)
+    for start in range(0, len(tokens) - block_size + 1, block_size):
+        node = next_identity(node, tokens[start:start + block_size])
+        ids.append(node)
+    return ids
+
+
+class KnownBlocks:
+    """A bare set of known full-block identities (no pool, no eviction):
+    what a lookup against everything ever registered would reuse."""
 
     def __init__(self, block_size: int):
         if block_size <= 0:
-            raise ValueError("block_size must be positive")
+            raise ValueError("block size must be positive")
         self.block_size = block_size
-        self.known = set()
+        self.ids = set()
 
-    def insert_sequence(self, tokens, namespace: str = "default") -> int:
-        """Register every full block of ``tokens``; returns how many."""
-        digests = chain(list(tokens), self.block_size, namespace)
-        self.known.update(digests)
-        return len(digests)
+    def add(self, tokens, scope: str = "default") -> int:
+        """Make every full block of ``tokens`` known; returns their count."""
+        ids = prefix_identities(list(tokens), self.block_size, scope)
+        self.ids.update(ids)
+        return len(ids)
 
-    def match_prefix(self, tokens, namespace: str = "default"):
-        """(cached tokens, fresh tokens): the longest run of known full
-        blocks from the start, then the rest."""
-        tokens = list(tokens)
-        n = 0
-        for d in chain(tokens, self.block_size, namespace):
-            if d not in self.known:
+    def hit_tokens(self, tokens, scope: str = "default") -> int:
+        """Tokens covered by the leading run of known full blocks."""
+        run = 0
+        for ident in prefix_identities(list(tokens), self.block_size, scope):
+            if ident not in self.ids:
                 break
-            n += 1
-        split = n * self.block_size
-        return tokens[:split], tokens[split:]
+            run += 1
+        return run * self.block_size

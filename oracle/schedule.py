@@ -21,11 +21,11 @@ the batch descriptor.  Plain Python, integer work only.
   3, "Cache granularity and eviction in preallocated pools"); the free count
   includes the reclaimable ones (same section, "Accounting considerations").
   Allocation takes empty blocks first and then evicts the least recently
-  freed cached block, unlinking its digest (eviction is host metadata only).
+  freed cached block, forgetting its identity (eviction is host metadata only).
   A request's prefix is looked up once, when it is first scheduled, and only
   over the blocks of that first chunk ("vLLM Chunked Prefill ...", section
   2.2 and the scenario of section 3.1); full blocks are registered under
-  their chained digest (``oracle.prefix_cache``) as their tokens are
+  their exact chained identity (``oracle.prefix_cache``) as their tokens are
   computed.
 """
 from __future__ import annotations
@@ -58,34 +58,31 @@ def schedule_prompt(max_batched_tokens: int, active_decodes: int, total_prompt_t
         raise ValueError("counts must be non-negative")
     if align_to_block and block_size <= 0:
         raise ValueError("block_size must be positive")
-    budget = max_batched_tokens - active_decodes
-    if budget <= 0:
-        raise BudgetExhausted(f"active_decodes ({active_decodes}) >= max_batched_tokens "
-                              f"({max_batched_tokens})")
-    chunks = []
-    remaining = total_prompt_tokens
-    while remaining > 0:
-        take = min(remaining, budget)
-        if align_to_block and take < remaining:
-            take = (take // block_size) * block_size
-            if take == 0:
-                raise BudgetExhausted(f"budget {budget} is below one block of {block_size}")
-        chunks.append(take)
-        remaining -= take
-    return chunks
+    room = max_batched_tokens - active_decodes      # prefill share of every step
+    if room <= 0:
+        raise BudgetExhausted("the decodes use the whole token budget")
+    if total_prompt_tokens <= room:                 # fits in one step (or nothing to do)
+        return [total_prompt_tokens] if total_prompt_tokens else []
+    # every step but the last fills the room (cut to whole blocks when
+    # aligning); the last takes what is left, which then fits the room
+    full = (room // block_size) * block_size if align_to_block else room
+    if full == 0:
+        raise BudgetExhausted("the prefill share of a step is below one block")
+    steps = cdiv(total_prompt_tokens - room, full)
+    return [full] * steps + [total_prompt_tokens - steps * full]
 
 
 class BlockPool:
     """Fixed pool of physical blocks: a FIFO list of empty blocks (in the
     given order), a reference count per block and, for prefix caching, the
-    digest a block holds, the digest table and the reclaimable cached blocks
+    identity a block holds, the identity table and the reclaimable cached blocks
     in the order they were freed."""
 
     def __init__(self, num_blocks: int, free_order=None):
         order = range(num_blocks) if free_order is None else [int(x) for x in free_order]
         self.free = deque(order)
         self.ref = [0] * num_blocks
-        self.digest = [None] * num_blocks
+        self.identity = [None] * num_blocks
         self.table = {}
         self.lru = OrderedDict()
 
@@ -111,8 +108,8 @@ class BlockPool:
                 blk = self.free.popleft()
             else:
                 blk, _ = self.lru.popitem(last=False)     # least recently freed cached block
-                del self.table[self.digest[blk]]
-                self.digest[blk] = None
+                del self.table[self.identity[blk]]
+                self.identity[blk] = None
             self.ref[blk] = 1
             out.append(blk)
         return out
@@ -129,19 +126,20 @@ class BlockPool:
             del self.lru[blk]
         self.ref[blk] += 1
 
-    def register(self, blk: int, digest: str) -> None:
-        """Block ``blk`` now holds the full block ``digest`` (first holder wins)."""
-        if digest not in self.table:
-            self.table[digest] = blk
-            self.digest[blk] = digest
+    def register(self, blk: int, ident: int) -> None:
+        """Block ``blk`` now holds the full block ``ident`` (first holder wins)."""
+        if ident not in self.table:
+            self.table[ident] = blk
+            self.identity[blk] = ident
 
-    def lookup(self, digests) -> list:
-        """Blocks of the longest run of known digests from the first."""
+    def lookup(self, idents) -> list:
+        """Blocks of the leading run of known identities."""
         out = []
-        for d in digests:
-            if d not in self.table:
+        for ident in idents:
+            blk = self.table.get(ident)
+            if blk is None:
                 break
-            out.append(self.table[d])
+            out.append(blk)
         return out
 
     def release(self, blocks) -> None:
@@ -154,10 +152,10 @@ class BlockPool:
             if self.ref[blk] == 0:
                 unused.append(blk)
         for blk in unused:
-            if self.digest[blk] is None:
+            if self.identity[blk] is None:
                 self.free.append(blk)
         for blk in reversed(unused):
-            if self.digest[blk] is not None:
+            if self.identity[blk] is not None:
                 self.lru[blk] = None
 
 
@@ -171,7 +169,7 @@ class Request:
         self.is_decode = is_decode
         self.tokens = None if tokens is None else [int(t) for t in tokens]   # prompt token ids
         self.namespace = namespace
-        self.digests = []                   # chained digests of its first full blocks
+        self.ids = []                       # identities of its first full blocks
         self.looked_up = False
 
 
@@ -287,9 +285,8 @@ class Scheduler:
                 # and leaves at least the prompt's last token to compute
                 first = self._take(r.num_tokens, used)
                 limit = min(first, r.num_tokens - 1) // self.block_size
-                digests = _pc.chain(r.tokens[:limit * self.block_size], self.block_size,
-                                    r.namespace)
-                hit = self.pool.lookup(digests)
+                hit = self.pool.lookup(_pc.prefix_identities(r.tokens[:limit * self.block_size],
+                                                             self.block_size, r.namespace))
                 computed = len(hit) * self.block_size
             take = self._take(r.num_tokens - computed, used)
             if take <= 0:
@@ -326,7 +323,7 @@ class Scheduler:
         r.num_computed = 0
         r.is_decode = False
         r.looked_up = False
-        r.digests = []
+        r.ids = []
 
     def step(self) -> dict:
         """Pick this step's tokens, grow the block tables, return the batch
@@ -357,7 +354,7 @@ class Scheduler:
                 self.pool.claim(b)
             r.blocks = list(hit)
             r.num_computed = len(hit) * self.block_size
-            r.digests = _pc.chain(r.tokens[:r.num_computed], self.block_size, r.namespace)
+            r.ids = _pc.prefix_identities(r.tokens[:r.num_computed], self.block_size, r.namespace)
         for (r, _), k in zip(picked, need_new):
             r.blocks.extend(self.pool.allocate(k))
         cu = [0]
@@ -391,14 +388,14 @@ class Scheduler:
         self._last = []
 
     def _register(self, r) -> None:
-        """Register the request's newly full prompt blocks under their digests."""
+        """Register the request's newly full prompt blocks under their identities."""
         bs = self.block_size
         full = min(r.num_computed, len(r.tokens)) // bs
-        for j in range(len(r.digests), full):
-            parent = r.digests[-1] if r.digests else _pc.ROOT
-            d = _pc.block_hash(parent, r.tokens[j * bs:(j + 1) * bs], r.namespace)
-            self.pool.register(r.blocks[j], d)
-            r.digests.append(d)
+        for j in range(len(r.ids), full):
+            parent = r.ids[-1] if r.ids else _pc.scope_root(r.namespace)
+            ident = _pc.next_identity(parent, r.tokens[j * bs:(j + 1) * bs])
+            self.pool.register(r.blocks[j], ident)
+            r.ids.append(ident)
 
     def free_request(self, req_id: int) -> None:
         r = self._find(req_id)

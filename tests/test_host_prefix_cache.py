@@ -158,7 +158,7 @@ def test_random_prefix_cached_runs_agree_with_oracle(seed):
             toks = [int(t) for t in sysp + suffix]
             ns = scopes[int(rng.integers(0, 2))]
             assert p.prod.prefix_match(toks, ns) == (
-                len(p.pool.lookup(opc.chain(toks, bs, ns))) * bs)
+                len(p.pool.lookup(opc.prefix_identities(toks, bs, ns))) * bs)
             p.add(next_id, toks, ns)
             live.append(next_id)
             next_id += 1

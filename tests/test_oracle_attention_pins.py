@@ -215,3 +215,57 @@ def test_cache_write_touches_exactly_the_active_slots():
     # offset 13 -> block 5; position 16 -> logical block 1 -> block 2, offset 0
     assert slots[0] == 5 * 16 + 13 and slots[3] == 2 * 16 + 0
     assert slots[20] == 11 * 16 + 8                # seq 1 position 40 -> block 11, offset 8
+
+
+# --------------------------------------------------------------------------
+# attention_rows: the sampled-row checker of the full-size runs
+# --------------------------------------------------------------------------
+def _rows_brute_force(qr, keys, vals, positions, scale):
+    """Pure-Python loops with math.exp: row i attends to keys 0..positions[i]."""
+    out = np.zeros((len(qr), vals.shape[1]))
+    for i, pos in enumerate(positions):
+        logits = [scale * sum(float(qr[i, d]) * float(keys[j, d]) for d in range(keys.shape[1]))
+                  for j in range(pos + 1)]
+        mx = max(logits)
+        w = [math.exp(x - mx) for x in logits]
+        z = sum(w)
+        for d in range(vals.shape[1]):
+            out[i, d] = sum(w[j] * float(vals[j, d]) for j in range(pos + 1)) / z
+    return out
+
+
+def test_attention_rows_brute_force():
+    # rows at the first key, the last key and in between, on large logits
+    # (scale 0.9 with N(0, 2^2) entries) so the max subtraction matters
+    L, D = 41, 8
+    keys, vals = 2 * _rand(201, L, D), _rand(202, L, D)
+    positions = [0, 1, 7, 16, 39, 40]
+    qr = 2 * _rand(203, len(positions), D)
+    got = oa.attention_rows(qr, keys, vals, positions, 0.9)
+    np.testing.assert_allclose(got, _rows_brute_force(qr, keys, vals, positions, 0.9),
+                               rtol=0, atol=1e-12)
+
+
+def test_attention_rows_zero_keys_prefix_mean():
+    # K = 0: every allowed logit is 0, so row i is the mean of V[0..positions[i]]
+    L, D = 300, 16
+    vals = _rand(211, L, D)
+    positions = [0, 5, 63, 64, 255, 299]
+    got = oa.attention_rows(_rand(212, len(positions), D), np.zeros((L, D)), vals, positions, 0.3)
+    expect = np.stack([vals[:p + 1].mean(axis=0) for p in positions])
+    np.testing.assert_allclose(got, expect, rtol=0, atol=1e-12)
+
+
+def test_attention_rows_selector_picks_value_row():
+    # q = alpha * k[tau] over random unit keys: O equals V[tau] (closed form),
+    # including tau equal to the row's own position (the inclusive diagonal)
+    L, D = 500, 128
+    rng = np.random.default_rng(221)
+    keys = rng.standard_normal((L, D))
+    keys /= np.linalg.norm(keys, axis=1, keepdims=True)
+    vals = rng.standard_normal((L, D))
+    positions = [0, 3, 100, 257, 499, 499]
+    tau = [0, 3, 17, 257, 0, 499]
+    qr = 2000.0 * keys[tau]
+    got = oa.attention_rows(qr, keys, vals, positions, 1 / math.sqrt(D))
+    np.testing.assert_allclose(got, vals[tau], rtol=0, atol=1e-12)

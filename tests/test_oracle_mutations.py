@@ -87,3 +87,52 @@ def test_planted_merge_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(oa, "partial_state", _partial_no_rescale)
     with pytest.raises(AssertionError):
         pins.test_brute_force_tiny_chunked_paged()
+
+
+# --------------------------------------------------------------------------
+# attention_rows (the checker of sampled rows at full size)
+# --------------------------------------------------------------------------
+_orig_rows = oa.attention_rows
+
+
+def _rows_strict(q_rows, keys, vals, positions, scale):
+    # the diagonal dropped: row i sees keys < positions[i] (position 0 keeps one key)
+    return _orig_rows(q_rows, keys, vals, [max(p - 1, 0) for p in positions], scale)
+
+
+def _rows_no_scale(q_rows, keys, vals, positions, scale):
+    return _orig_rows(q_rows, keys, vals, positions, 1.0)
+
+
+def _rows_one_past(q_rows, keys, vals, positions, scale):
+    # one key too many (clamped to the keys given)
+    return _orig_rows(q_rows, keys, vals, [min(p + 1, len(keys) - 1) for p in positions], scale)
+
+
+def _rows_values_reversed(q_rows, keys, vals, positions, scale):
+    # values read in the wrong order (a transposed or flipped gather)
+    return _orig_rows(q_rows, keys, np.asarray(vals)[::-1], positions, scale)
+
+
+ROW_PINS = [
+    pins.test_attention_rows_brute_force,
+    pins.test_attention_rows_zero_keys_prefix_mean,
+    pins.test_attention_rows_selector_picks_value_row,
+]
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("diagonal dropped", _rows_strict),
+    ("scale dropped", _rows_no_scale),
+    ("one key past the position", _rows_one_past),
+    ("values reversed", _rows_values_reversed),
+])
+def test_planted_attention_rows_mistake_is_caught(monkeypatch, name, bad):
+    monkeypatch.setattr(oa, "attention_rows", bad)
+    failures = 0
+    for pin in ROW_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1, f"no pin caught: {name}"

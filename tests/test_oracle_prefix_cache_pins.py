@@ -13,30 +13,38 @@ GOLD = {r[0]: (int(r[1]), kv(r[2])) for r in rows("prefix_cache.txt")}
 
 def test_pot_standalone_matching():
     bs, exp = GOLD["pot_test1"]
-    cache = opc.PrefixCache(bs)
+    cache = opc.KnownBlocks(bs)
     base = list(range(1, 2501))
-    assert cache.insert_sequence(base, "model_shared") == int(exp["inserted"])
-    cached, fresh = cache.match_prefix(base + list(range(5000, 5500)), "model_shared")
-    assert (len(cached), len(fresh)) == (int(exp["cached"]), int(exp["fresh"]))
+    assert cache.add(base, "model_shared") == int(exp["inserted"])
+    query = base + list(range(5000, 5500))
+    hit = cache.hit_tokens(query, "model_shared")
+    assert (hit, len(query) - hit) == (int(exp["cached"]), int(exp["fresh"]))
     bs, exp = GOLD["pot_test2"]
     seq = list(range(100, 164))
-    cache.insert_sequence(seq, "model_shared")
+    cache.add(seq, "model_shared")
     mutated = list(seq)
     mutated[5] = 999999
-    cached, fresh = cache.match_prefix(mutated, "model_shared")
-    assert (len(cached), len(fresh)) == (int(exp["cached"]), int(exp["fresh"]))
+    hit = cache.hit_tokens(mutated, "model_shared")
+    assert (hit, len(mutated) - hit) == (int(exp["cached"]), int(exp["fresh"]))
     bs, exp = GOLD["pot_test3"]
-    cached, _ = cache.match_prefix(base, "tenant_isolated")
-    assert len(cached) == int(exp["cached"])
+    assert cache.hit_tokens(base, "tenant_isolated") == int(exp["cached"])
 
 
-def test_one_changed_token_changes_every_later_digest():
+def test_one_changed_token_changes_every_later_identity():
     a = list(range(64))
     b = list(a)
     b[5] = 7777
-    da, db = opc.chain(a, 16, "ns"), opc.chain(b, 16, "ns")
-    assert all(x != y for x, y in zip(da, db))
-    assert opc.chain(a, 16, "ns") == da and opc.chain(a, 16, "other") != da
+    da, db = opc.prefix_identities(a, 16, "ns"), opc.prefix_identities(b, 16, "ns")
+    assert len(da) == 4 and all(x != y for x, y in zip(da, db))
+    assert opc.prefix_identities(a, 16, "ns") == da
+    assert not set(opc.prefix_identities(a, 16, "other")) & set(da)
+    # a change in the last block leaves the earlier identities alone
+    c = list(a)
+    c[63] = 1
+    dc = opc.prefix_identities(c, 16, "ns")
+    assert dc[:3] == da[:3] and dc[3] != da[3]
+    # only full blocks have an identity
+    assert len(opc.prefix_identities(a[:63], 16, "ns")) == 3
 
 
 def _run(sched, rid):
@@ -100,7 +108,7 @@ def test_kvm_first_chunk_only_scenario():
         s.commit()
     assert computed == int(exp["b_computed"])
     # A's blocks for tokens 2048..4095 are still cached, unused by B
-    assert all(pool.digest[x] is not None and pool.ref[x] == 0 for x in a_blocks[hit:256])
+    assert all(pool.identity[x] is not None and pool.ref[x] == 0 for x in a_blocks[hit:256])
 
 
 def test_three_buckets_partition_the_pool():
@@ -140,15 +148,17 @@ def test_lru_eviction_trace():
 # --------------------------------------------------------------------------
 # planted mistakes
 # --------------------------------------------------------------------------
-def _hash_without_parent(parent, block_tokens, namespace):
-    return _orig_hash("ROOT", block_tokens, namespace)
+def _identity_without_parent(parent, block_tokens):
+    # every block hangs off one root: content alone identifies it
+    return _orig_next(-7, block_tokens)
 
 
-def _hash_without_namespace(parent, block_tokens, namespace):
-    return _orig_hash(parent, block_tokens, "")
+def _root_without_scope(scope):
+    return _orig_root("default")
 
 
-_orig_hash = opc.block_hash
+_orig_next = opc.next_identity
+_orig_root = opc.scope_root
 
 
 def _release_mru(self, blocks):
@@ -158,7 +168,7 @@ def _release_mru(self, blocks):
         if self.ref[blk] == 0:
             unused.append(blk)
     for blk in unused:
-        if self.digest[blk] is None:
+        if self.identity[blk] is None:
             self.free.append(blk)
         else:
             self.lru[blk] = None
@@ -168,13 +178,13 @@ def _release_mru(self, blocks):
 def test_block_content_at_another_position_does_not_match():
     # the chain, not the content alone, identifies a block: a query whose
     # first block equals a registered second block matches nothing
-    cache = opc.PrefixCache(4)
-    cache.insert_sequence([1, 2, 3, 4, 5, 6, 7, 8], "ns")
-    cached, _ = cache.match_prefix([5, 6, 7, 8, 9], "ns")
-    assert cached == []
+    cache = opc.KnownBlocks(4)
+    cache.add([1, 2, 3, 4, 5, 6, 7, 8], "ns")
+    assert cache.hit_tokens([5, 6, 7, 8, 9], "ns") == 0
+    assert cache.hit_tokens([1, 2, 3, 4, 5, 6, 7, 8, 9], "ns") == 8
 
 
-PINS = [test_one_changed_token_changes_every_later_digest,
+PINS = [test_one_changed_token_changes_every_later_identity,
         test_block_content_at_another_position_does_not_match,
         test_pot_standalone_matching, test_pot_matching_through_the_scheduler,
         test_kvm_first_chunk_only_scenario, test_three_buckets_partition_the_pool,
@@ -182,8 +192,8 @@ PINS = [test_one_changed_token_changes_every_later_digest,
 
 
 @pytest.mark.parametrize("name,target,attr,bad", [
-    ("digest ignores the parent", opc, "block_hash", _hash_without_parent),
-    ("digest ignores the namespace", opc, "block_hash", _hash_without_namespace),
+    ("identity ignores the parent", opc, "next_identity", _identity_without_parent),
+    ("identity ignores the scope", opc, "scope_root", _root_without_scope),
     ("most recently freed evicted first", osch.BlockPool, "release", _release_mru),
 ])
 def test_planted_prefix_cache_mistake_is_caught(monkeypatch, name, target, attr, bad):

@@ -188,3 +188,39 @@ def test_chunk_bytes_components():
     b0 = oc.chunk_bytes(2048, 0, 32, 8, 128, 2)
     b1 = oc.chunk_bytes(2048, 8192, 32, 8, 128, 2)
     assert b1 - b0 == 8192 * oc.kv_bytes_per_token(8, 128, 2)
+
+
+def _check_chunk_bytes(fn):
+    """Every term of the algorithmic bytes of a chunk, evaluated by hand for
+    the 10k prompt's five chunks (G=8 KV heads, H=32, D=128, 2-byte
+    elements): Q read 8192 B/token, new K and V read 4096 B/token and
+    written to the cache 4096 B/token, cached K and V read 4096 B per cached
+    token, O written 8192 B/token."""
+    per_new = 8192 + 4096 + 4096 + 8192          # 24,576 B per active token
+    per_cached = 4096
+    hand = {(2048, 0): 50_331_648, (2048, 2048): 58_720_256, (2048, 4096): 67_108_864,
+            (2048, 6144): 75_497_472, (1808, 8192): 77_987_840}
+    for (n, c), total in hand.items():
+        assert n * per_new + c * per_cached == total
+        assert fn(n, c, 32, 8, 128, 2) == total
+    # one token, nothing cached, H=1, G=1, D=1, 1-byte elements: Q, K, V,
+    # the two cache writes and O are one byte each
+    assert fn(1, 0, 1, 1, 1, 1) == 6
+    # query heads touch only Q and O; KV heads only the K/V terms
+    assert fn(10, 7, 3, 1, 1, 1) == 10 * 3 * 2 + 10 * 4 + 7 * 2
+    assert fn(0, 7, 3, 1, 1, 1) == 14
+
+
+def test_chunk_bytes_hand_evaluated():
+    _check_chunk_bytes(oc.chunk_bytes)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("O write dropped", lambda n, c, H, G, D, e: oc.chunk_bytes(n, c, H, G, D, e) - n * H * D * e),
+    ("cache write dropped", lambda n, c, H, G, D, e: oc.chunk_bytes(n, c, H, G, D, e) - 2 * n * G * D * e),
+    ("cached V not counted", lambda n, c, H, G, D, e: oc.chunk_bytes(n, c, H, G, D, e) - c * G * D * e),
+    ("Q sized by KV heads", lambda n, c, H, G, D, e: oc.chunk_bytes(n, c, H, G, D, e) - n * (H - G) * D * e),
+])
+def test_planted_chunk_bytes_mistake_is_caught(name, bad):
+    with pytest.raises(AssertionError):
+        _check_chunk_bytes(bad)

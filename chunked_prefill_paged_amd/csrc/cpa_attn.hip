@@ -78,6 +78,12 @@ __device__ inline void gather16(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
+// the same with the LDS slab address formed in M0 itself (lds0 + a constant)
+template <int OFF>
+__device__ inline void gather16_at(const void* base, uint32_t voff, uint32_t lds0) {
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds0), "i"(OFF) : "memory", "m0");
+}
 // per-lane 64-bit address
 __device__ inline void gather16(const void* addr, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
@@ -306,6 +312,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
         const int rk = (wave * NLD + i) * RK + lane / NCK;
         k_dma_off[i] = (lane / NCK) * D + ((lane % NCK) ^ (swap_bits23(rk & 31) & SWK)) * EPC;
     }
+    // When a wave's NLD slabs (NLD * RK consecutive keys) lie in one block
+    // (block_size >= NLD * RK), one scalar base per tile serves all of them:
+    // slab i is then i * RK rows further, folded into its lane offset.
+    constexpr int KRUN = NLD * RK;
+    uint32_t k_run_off[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) k_run_off[i] = (uint32_t)((k_dma_off[i] + i * RK * D) * (int)sizeof(T));
     const int v_d0 = wave * NLD * RV + lane / NCV;
     auto v_dma_key = [&](int i) {
         const int d = v_d0 + i * RV;
@@ -325,6 +338,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     const uint32_t blk_bytes = (uint32_t)(G * bs * D * (int)sizeof(T));
     auto dma_k = [&](int ts, int buf, int btv) {
         const uint32_t lds0 = lds_addr(&lds_k[buf][0]);
+        if (bs >= KRUN) {
+            const int kr = wave * KRUN;                    // first key of the wave's run
+            const uint32_t blk = min((uint32_t)__builtin_amdgcn_readlane(btv, bs >= kKeys ? 0 : (kr >> lbs)), nb_max);
+            const char* base = kc_g + (size_t)blk * blk_bytes + ((ts + kr) & (bs - 1)) * (D * (int)sizeof(T));
+            const uint32_t l0 = lds0 + wave * NLD * 1024;
+            gather16_at<0>(base, k_run_off[0], l0);
+            if constexpr (NLD > 1) gather16_at<1024>(base, k_run_off[1], l0);
+            if constexpr (NLD > 2) gather16_at<2048>(base, k_run_off[2], l0);
+            if constexpr (NLD > 3) gather16_at<3072>(base, k_run_off[3], l0);
+            static_assert(NLD <= 4, "at most four slabs per wave");
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int sl = wave * NLD + i;
@@ -340,12 +365,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             // the 64 keys of the tile share one block: scalar base, 32-bit lane offsets
             const uint32_t blk = min((uint32_t)__builtin_amdgcn_readlane(btv, 0), nb_max);
             const char* base = vc_g + (size_t)blk * blk_bytes + (ts & (bs - 1)) * (int)sizeof(T);
-#pragma unroll
-            for (int i = 0; i < NLD; ++i) {
-                const int sl = wave * NLD + i;
-                const uint32_t off = (uint32_t)(((v_d0 + i * RV) * bs + v_dma_key(i)) * (int)sizeof(T));
-                gather16(base, off, lds0 + sl * 1024);
-            }
+            const uint32_t l0 = lds0 + wave * NLD * 1024;
+            auto off = [&](int i) { return (uint32_t)(((v_d0 + i * RV) * bs + v_dma_key(i)) * (int)sizeof(T)); };
+            gather16_at<0>(base, off(0), l0);
+            if constexpr (NLD > 1) gather16_at<1024>(base, off(1), l0);
+            if constexpr (NLD > 2) gather16_at<2048>(base, off(2), l0);
+            if constexpr (NLD > 3) gather16_at<3072>(base, off(3), l0);
         } else {
 #pragma unroll
             for (int i = 0; i < NLD; ++i) {

@@ -547,22 +547,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             for (int r = 0; r < 16; ++r) {
                 const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[sub][r], sl2e, nm));
                 S[sub][r] = pv;
-                rs += pv;
+                if constexpr (KPL != 8) rs += pv;
             }
         }
-        l_run += rs;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             if constexpr (KPL == 8) {
+                // bf16 weights: the row sum adds the rounded values the PV
+                // product uses
                 const int sub = ks >> 1, r0 = (ks & 1) * 8;
                 bf16x8 v;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = (__bf16)S[sub][r0 + i];
+                for (int i = 0; i < 8; ++i) {
+                    v[i] = (__bf16)S[sub][r0 + i];
+                    rs += (float)v[i];
+                }
                 pf[ks] = v;
             } else {
                 pf[ks] = S[ks >> 4][ks & 15];
             }
         }
+        l_run += rs;
     };
     // O^T += V^T P^T from V buffer vbuf
     auto pv = [&](int vbuf, const Frag (&pf)[NKS]) {
@@ -592,10 +597,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     // tiles of 32 keys (tiles on the causal diagonal, at a split end or at
     // the sequence end first mask their scores to -inf).  LDS fragments are prefetched three MFMAs ahead through four
     // rotating registers; sched_barrier fences pin the order:
-    //   P1  S0 = K[0:32] Q^T - m2   (8 MFMAs)
-    //   P2  S1 = K[32:64] Q^T - m2  (8 MFMAs)  || exp, sum, convert of S0, then S0's check
+    //   P1  S0 = K[0:32] Q^T        (8 MFMAs)
+    //   P2  S1 = K[32:64] Q^T       (8 MFMAs)  || exp, sum, convert of S0, then S0's check
     //   P3  O += V[0:32] P0         (8 MFMAs)  || exp, sum, convert of S1, then S1's check
-    //   P4  O += V[32:64] P1        (8 MFMAs)  || the next tile's -m2 presets
+    //   P4  O += V[32:64] P1        (8 MFMAs)
     // The reference maximum of a row moves only when the 16 exps of some
     // lane's share of a 32-key block sum past 2^12, so that one of them
     // exceeds 2^8: the common path takes no maximum and needs no exchange
@@ -616,10 +621,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
         v_base = (uint32_t)(lrow * kKeys * 2 + (half ^ (swl & 1)) * 16);
         v_x = (uint32_t)((swl & 6) * 16);
     }
-    // The hand-ordered path's score accumulators: each QK chain starts from
-    // -m2 (set for the next tile once a tile's last check has passed), and
-    // the queries carry scale * log2(e), so the MFMAs leave the exp2
-    // arguments t = S * scale * log2(e) - m2 themselves.
+    // The hand-ordered path's raw score accumulators (each QK chain starts
+    // from zero).  The softmax scale is applied in float to every score, in
+    // the FMA that forms its exp2 argument t = S * scale * log2(e) - m2:
+    // folding it into bf16 queries instead would round q * scale once more,
+    // a logit error of about 2^-9 * scale * |q| |k| that peaked softmaxes
+    // (large logits) turn into output errors beyond the bf16 tolerance.
     f32x16 S0 = {}, S1 = {};
     auto compute_tile = [&](int buf, int ts, bool masked) {
         if constexpr (kHandOrdered) {
@@ -637,6 +644,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             bf16x8 fr[4];
             u32x4 pw[4];
             float rs = 0.f;
+            const bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
             // causal / split-end mask of one 32-key block (register r holds
             // key ts + blk*32 + 16*(r/8) + 8*half + r%8)
             auto apply_mask = [&](f32x16& S, int blk) {
@@ -646,11 +654,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                     if (j > lim || j >= k1) S[r] = -INFINITY;
                 }
             };
-            // S0 and S1 hold exp2 arguments t = S * scale * log2(e) - m2 (m2:
-            // the row's reference maximum in log2 units, taken as 0 while
-            // unset).  The rare path's maximum is taken on t: MFMA results
-            // need no NaN quieting here, so one v_max3 folds two scores.
+            // S0 and S1 hold raw scores; their exp2 arguments are t = S *
+            // scale * log2(e) - m2 (m2: the row's reference maximum in log2
+            // units, taken as 0 while unset).  The rare path's maximum is taken
+            // on S: MFMA results need no NaN quieting here, so one v_max3
+            // folds two scores.
             auto ref_nm = [&]() { return (m2 == -INFINITY) ? 0.f : -m2; };
+            float nm = ref_nm();
             // one v_max3 per score pair, chained (the compiler otherwise
             // builds a tree of two-input maxima)
             auto max3 = [](float a, float b, float c) {
@@ -663,10 +673,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             // speculative exp that a rescale recomputes would otherwise be
             // sunk by the compiler past the decision, out of its MFMA phase)
             auto ex2 = [&](const f32x16& S, int ks, int r) {
-                const float e0 = __builtin_amdgcn_exp2f(S[r]);
-                const float e1 = __builtin_amdgcn_exp2f(S[r + 1]);
-                rs += e0 + e1;
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], sl2e, nm));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r + 1], sl2e, nm));
                 const bf16x2 pk = {(__bf16)e0, (__bf16)e1};
+                // the row sum adds the rounded weights the PV product uses,
+                // so that a dominant key's rounding cancels in O / l
+                rs = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnes2, rs, false);
                 const uint32_t w = __builtin_bit_cast(uint32_t, pk);
                 asm volatile("" :: "v"(w), "v"(rs));
                 pw[ks][(r & 7) >> 1] = w;
@@ -676,17 +688,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             auto over = [&](float sum, float cap) {
                 return __builtin_amdgcn_ballot_w64(m2 == -INFINITY || sum > cap) != 0;
             };
-            // the lane's maximum t over registers [r0, 16) of a block
+            // the lane's maximum raw score over registers [r0, 16) of a block
             auto tmax = [&](const f32x16& S, int r0) {
                 float ht = -INFINITY;
 #pragma unroll
                 for (int r = r0; r < 16; r += 2) ht = max3(ht, S[r], S[r + 1]);
                 return ht;
             };
-            // raise those references to the row maximum, rescaling O and l;
-            // returns the lane's shift of t
-            auto decide = [&](float ht) -> float {
-                const float pt = fmaxf(ht, __shfl_xor(ht, 32));
+            // raise those references to the row maximum (t of the largest
+            // score), rescaling O and l; nm follows the new reference
+            auto decide = [&](float hs) {
+                const float ps = fmaxf(hs, __shfl_xor(hs, 32));
+                const float pt = __builtin_fmaf(ps, sl2e, nm);   // -inf stays -inf
                 const bool g = (m2 == -INFINITY) ? pt > -INFINITY : pt > 8.f;
                 const float m_new = g ? ((m2 == -INFINITY) ? 0.f : m2) + pt : m2;
                 const float alpha = g ? __builtin_amdgcn_exp2f(m2 - m_new) : 1.f;
@@ -694,11 +707,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
 #pragma unroll
                 for (int i = 0; i < NDT; ++i) oacc[i] *= alpha;
                 m2 = m_new;
-                return g ? pt : 0.f;
+                nm = ref_nm();
             };
             fr[0] = frag(0);
             fr[1] = frag(1);
             fr[2] = frag(2);
+            S0 = f32x16{};
+            S1 = f32x16{};
             __builtin_amdgcn_sched_barrier(0);
             // P1
 #pragma unroll
@@ -712,8 +727,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             // Speculative exps: a block's exps use the current reference
             // before the block is checked; when the check fails (rare; always
             // while some row of the wave has no reference, as on an item's
-            // first tile), the block's t are shifted and its exps redone
-            // after the rescale.
+            // first tile), the block's exps are redone under the new
+            // reference.
             // P2: S1 MFMAs; exps of S0
 #pragma unroll
             for (int f = 8; f < 16; ++f) {
@@ -724,16 +739,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (over(rs, 4096.f)) {
-                const float sh = decide(tmax(S0, 0));
+                decide(tmax(S0, 0));
                 rs = 0.f;
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    S0[r] -= sh;
-                    S0[r + 1] -= sh;
-                    ex2(S0, r >> 3, r);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) S1[r] -= sh;   // started from the old -m2 too
+                for (int r = 0; r < 16; r += 2) ex2(S0, r >> 3, r);
             }
             l_run += rs;                 // before S1's decision may rescale l
             rs = 0.f;
@@ -748,37 +757,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (over(rs, 4096.f)) {
-                const float sh = decide(tmax(S1, 0));
+                decide(tmax(S1, 0));
                 rs = 0.f;
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    S1[r] -= sh;
-                    S1[r + 1] -= sh;
-                    ex2(S1, 2 + (r >> 3), r);
-                }
+                for (int r = 0; r < 16; r += 2) ex2(S1, 2 + (r >> 3), r);
             }
             l_run += rs;
             __builtin_amdgcn_sched_barrier(0);
-            // P4: PV of the second half; the reference is final for this
-            // tile, so the next tile's accumulators are preset under it (as
-            // pairs: one 64-bit move sets two registers)
-            typedef uint64_t u64x8 __attribute__((ext_vector_type(8)));
-            const uint64_t nb = __builtin_bit_cast(uint32_t, ref_nm());
-            const uint64_t n2 = (nb << 32) | nb;
-            u64x8 z0 = __builtin_bit_cast(u64x8, S0), z1 = __builtin_bit_cast(u64x8, S1);
+            // P4: PV of the second half
 #pragma unroll
             for (int i = 8; i < 16; ++i) {
                 if (i + 3 < 16) fr[(i + 3) & 3] = frag(16 + i + 3);
                 oacc[i & 3] = E::mma(fr[i & 3], __builtin_bit_cast(bf16x8, pw[i >> 2]), oacc[i & 3]);
-                uint64_t x0, x1;
-                asm volatile("v_mov_b64 %0, %1" : "=v"(x0) : "v"(n2));
-                asm volatile("v_mov_b64 %0, %1" : "=v"(x1) : "v"(n2));
-                z0[i - 8] = x0;
-                z1[i - 8] = x1;
                 __builtin_amdgcn_sched_barrier(0);
             }
-            S0 = __builtin_bit_cast(f32x16, z0);
-            S1 = __builtin_bit_cast(f32x16, z1);
         }
     };
 
@@ -813,14 +805,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             if (nfull > 1) btn = load_bt(tstart(1));
         }
         wait_vmem();                     // Q and the first block ids
-        if constexpr (kHandOrdered) {
-            // queries times scale * log2(e), rounded to bf16 once per item
-#pragma unroll
-            for (int f = 0; f < NQF; ++f) {
-#pragma unroll
-                for (int e = 0; e < KPL; ++e) qf[f][e] = (T)((float)qf[f][e] * sl2e);
-            }
-        }
         for (int u = 0; u < ntiles; ++u) {
             const int ts = tstart(u);
             const int buf = u & 1;
@@ -1153,7 +1137,7 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
             slot = p.slots[tok];
         } else {
             const int col = pos >> p.log2_bs;
-            slot = col < p.max_blocks
+            slot = (col >= 0 && col < p.max_blocks)
                        ? (int64_t)p.block_table[(size_t)seq * p.max_blocks + col] * bs + (pos & (bs - 1))
                        : -1;
         }
@@ -1547,6 +1531,26 @@ cpa_status check_pointers(const cpa_attn_args* a, bool attention) {
     return CPA_OK;
 }
 
+// Host mirrors of the descriptor, when a cache-write entry point is given
+// them: cu_seqlens_q starts at 0, ends at total_q and never decreases, no
+// cached length is negative, and without a slot mapping every sequence's
+// positions fit a block-table row (the checks resolve() makes for attention).
+cpa_status check_host_mirrors(const cpa_attn_args* a) {
+    if (!a->h_cu_seqlens_q || !a->h_cached_seq_len) return CPA_OK;
+    if (a->num_seqs <= 0) return CPA_ERR_INVALID_ARG;
+    const int32_t* cu = a->h_cu_seqlens_q;
+    if (cu[0] != 0 || cu[a->num_seqs] != a->total_q) return CPA_ERR_INVALID_ARG;
+    for (int b = 0; b < a->num_seqs; ++b) {
+        if (cu[b + 1] < cu[b] || a->h_cached_seq_len[b] < 0) return CPA_ERR_INVALID_ARG;
+        // slots derived from the table: the positions must fit a table row
+        if (!a->slot_mapping &&
+            ((int64_t)a->h_cached_seq_len[b] + cu[b + 1] - cu[b] + a->block_size - 1) / a->block_size >
+                a->max_blocks_per_seq)
+            return CPA_ERR_INVALID_ARG;
+    }
+    return CPA_OK;
+}
+
 inline bool kv_fp8(const cpa_attn_args* a) { return a->kv_dtype == CPA_FP8_E4M3; }
 
 inline float scale_or_one(float s) { return s == 0.f ? 1.f : s; }
@@ -1803,6 +1807,7 @@ cpa_status cpa_reshape_and_cache(const cpa_attn_args* a, void* stream) {
     cpa_status st = check_common(a);
     if (st != CPA_OK) return st;
     if ((st = check_pointers(a, false)) != CPA_OK) return st;
+    if ((st = check_host_mirrors(a)) != CPA_OK) return st;
     Resolved r{};
     return prep_dispatch(a, &r, false, nullptr, (hipStream_t)stream);
 }
@@ -1846,6 +1851,7 @@ cpa_status cpa_rope_reshape_and_cache(const cpa_attn_args* a, const cpa_rope_arg
     cpa_status st = check_common(a);
     if (st != CPA_OK) return st;
     if ((st = check_pointers(a, false)) != CPA_OK) return st;
+    if ((st = check_host_mirrors(a)) != CPA_OK) return st;
     if ((st = check_rope(a, rope)) != CPA_OK) return st;
     Resolved r{};
     return prep_dispatch(a, &r, false, rope, (hipStream_t)stream);

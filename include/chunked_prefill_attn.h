@@ -22,10 +22,11 @@
  *     null stream) and the call returns at once.
  *   - Errors are returned as cpa_status codes.  Only host-visible arguments
  *     are validated (dimensions, host mirrors of the lengths); device-resident
- *     values (block ids, slots) are preconditions.  Kernels skip any block id
- *     outside [0, num_blocks) and any slot outside [0, num_blocks*block_size)
- *     instead of touching memory there, so a bad table gives wrong results,
- *     never an out-of-bounds access.
+ *     values (block ids, slots) are preconditions.  The attention kernel
+ *     clamps a block id outside [0, num_blocks) to num_blocks - 1 (it reads
+ *     that block instead), and the cache write skips a slot outside
+ *     [0, num_blocks*block_size) and a block-table column outside the row, so
+ *     a bad table gives wrong results, never an out-of-bounds access.
  *
  * Device layouts (dtype = element type; row-major, innermost last)
  *   q        [total_q, num_heads,    head_dim]

@@ -143,11 +143,14 @@ class Pair:
     pool, driven in lockstep."""
 
     def __init__(self, num_blocks, num_kv_heads, block_size, head_dim, dtype, budget, max_blocks,
-                 free_order=None, fill=0.0, cap=0, align=False):
+                 free_order=None, fill=0.0, cap=0, align=False, prefix_caching=False,
+                 preemption=False):
         self.bs, self.dtype = block_size, dtype
-        self.prod = HostScheduler(num_blocks, block_size, budget, max_blocks, cap, align, free_order)
+        self.prod = HostScheduler(num_blocks, block_size, budget, max_blocks, cap, align, free_order,
+                                  prefix_caching=prefix_caching, preemption=preemption)
         self.pool = osch.BlockPool(num_blocks, free_order)
-        self.orc = osch.Scheduler(self.pool, block_size, budget, max_blocks, cap, align)
+        self.orc = osch.Scheduler(self.pool, block_size, budget, max_blocks, cap, align,
+                                  prefix_caching=prefix_caching, preemption=preemption)
         self.cache = GpuCache(num_blocks, num_kv_heads, block_size, head_dim, dtype, fill)
         shape = (num_blocks, block_size, num_kv_heads, head_dim)
         self.k_pool = np.full(shape, fill, dtype=np.float64)
@@ -182,10 +185,15 @@ class Pair:
         self.k_pool, self.v_pool = oa.cache_write(self.k_pool, self.v_pool, k64, v64, [r.blocks],
                                                   [0, L], [0], self.bs)
 
+    def add_request_tokens(self, rid, tokens, namespace="default"):
+        self.prod.add_request_tokens(rid, tokens, namespace)
+        self.orc.add_request_tokens(rid, tokens, namespace)
+
     def step(self):
         pb = self.prod.step()
         ob = self.orc.step()
         same_batches(pb, ob)
+        assert self.prod.last_preempted() == self.orc.preempted
         return pb, ob
 
     def commit(self):

@@ -110,6 +110,22 @@ def test_bad_host_mirrors_are_refused():
     assert _plan(a)[0] == _lib.CPA_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("over", [
+    {"cu": [0, 100, 299]},                 # does not end at total_q
+    {"cu": [1, 100, 300]},                 # does not start at 0
+    {"cu": [0, 200, 100], "total_q": 100}, # decreasing
+    {"cached": [-1, 0]},                   # negative cached length
+    {"cached": [4000, 0]},                 # 4100 tokens need 257 blocks > 200 per row
+])
+def test_cache_write_refuses_bad_host_mirrors(over):
+    # the cache-write entry points check the host mirrors they are given the
+    # way attention calls do, before any launch
+    a, _k = _args(slot_mapping=0, **over)
+    assert _lib.lib().cpa_reshape_and_cache(ctypes.byref(a), None) == _lib.CPA_ERR_INVALID_ARG
+    p = ctypes.byref(_rope())
+    assert _lib.lib().cpa_rope_reshape_and_cache(ctypes.byref(a), p, None) == _lib.CPA_ERR_INVALID_ARG
+
+
 def test_missing_workspace_is_refused_before_launch():
     a, _keep = _args()
     a.workspace, a.workspace_bytes = 0, 0

@@ -1,7 +1,8 @@
 """GPU parity on the five workloads at their full sizes.  Configs 1-3 are
-checked against the oracle on every output (config 2 and 3 on a subset of
-heads); configs 4 and 5 on sampled rows the oracle computes one by one, plus
-properties that hold at any size."""
+checked against the oracle on every output of every head (config 2 also
+through the exact path bench.py times); configs 4 and 5 on sampled rows the
+oracle computes one by one (all heads for config 4, one head of every KV
+group and more for config 5), plus properties that hold at any size."""
 import math
 
 import numpy as np
@@ -63,9 +64,9 @@ def test_config2_full_and_segment_sweep():
     need_gpu()
     w = get_workload("c2")
     heads = list(range(4)) + list(range(28, 32))          # KV groups 0 and 7
-    say("config 2, S=1024 vs oracle")
-    base, ref, pair = _chunked_prompt(w, 1024, heads=heads)
-    assert_close(base[:, heads], ref[:, heads], "bf16", "c2 S=1024")
+    say("config 2, S=1024 vs oracle, every head")
+    base, ref, pair = _chunked_prompt(w, 1024)
+    assert_close(base, ref, "bf16", "c2 S=1024")
     gk, gv = pair.cache.canonical_bits()
     assert np.array_equal(gk, bits_of(pair.k_pool, "bf16"))
     assert np.array_equal(gv, bits_of(pair.v_pool, "bf16"))
@@ -76,6 +77,48 @@ def test_config2_full_and_segment_sweep():
             got, _, _ = _chunked_prompt(w, S, split_pre=split, with_oracle=False)
             assert_close(got[:, heads], ref[:, heads], "bf16", f"c2 S={S} split={split} vs oracle")
             assert_close(got, base, "bf16", f"c2 S={S} split={split} vs S=1024")
+
+
+def test_config2_timed_path_every_head():
+    """The exact path bench.py times: the 10k prompt through the library's
+    host scheduler, the descriptor inline in the prepare launch's arguments,
+    slots derived from the block table, the automatic (folded) plan; every
+    output of every head against the oracle run chunk by chunk with its own
+    scheduler, and every cache bit."""
+    need_gpu()
+    import bench
+    w = get_workload("c2")
+    pb = bench.PromptBench(1024, 0, workload="c2")
+    assert pb.inline
+    say("config 2 through the timed path")
+    pb.step()
+    torch.cuda.synchronize()
+    got = pb.out.to(torch.float64).cpu().numpy()
+    q32, k32, v32 = prompt_qkv(w)
+    _, q64 = quantize(q32, "bf16")
+    _, k64 = quantize(k32, "bf16")
+    _, v64 = quantize(v32, "bf16")
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    kp, vp = np.zeros(shape), np.zeros(shape)
+    max_blocks = -(-w.prompt_len // w.block_size)
+    orc = osch.Scheduler(osch.BlockPool(w.num_blocks, free_block_order(w.num_blocks, w.seed)),
+                         w.block_size, w.max_batched_tokens, max_blocks)
+    orc.add_request(0, w.prompt_len)
+    pos = 0
+    while pos < w.prompt_len:
+        ob = orc.step()
+        n = ob["num_tokens"]
+        kp, vp = oa.cache_write(kp, vp, k64[pos:pos + n], v64[pos:pos + n], ob["block_table"],
+                                ob["cu_seqlens_q"], ob["cached_seq_len"], w.block_size)
+        ref = oa.attention(q64[pos:pos + n], kp, vp, ob["block_table"], ob["cu_seqlens_q"],
+                           ob["cached_seq_len"], w.block_size, w.scale, w.num_kv_heads)
+        assert_close(got[pos:pos + n], ref, "bf16", f"c2 timed path chunk at {pos}")
+        orc.commit()
+        pos += n
+    gk = pb.k_cache.view(torch.int16).permute(0, 2, 1, 3).contiguous().cpu().numpy()
+    gv = pb.v_cache.view(torch.int16).permute(0, 3, 1, 2).contiguous().cpu().numpy()
+    assert np.array_equal(gk, bits_of(kp, "bf16"))
+    assert np.array_equal(gv, bits_of(vp, "bf16"))
 
 
 def test_config3_prefix_shared_blocks():
@@ -121,7 +164,7 @@ def test_config3_prefix_shared_blocks():
         keys = np.concatenate([kp64, k64[cu[i]:cu[i + 1]]])
         vals = np.concatenate([vp64, v64[cu[i]:cu[i + 1]]])
         pos = prefix + np.arange(int(s))
-        for h in (0, 1, 2, 3, 17, 31):
+        for h in range(H):
             g = h // (H // G)
             ref = oa.attention_rows(q64[cu[i]:cu[i + 1], h], keys[:, g], vals[:, g], pos, w.scale)
             assert_close(got[cu[i]:cu[i + 1], h], ref, "bf16", f"c3 req {i} head {h}")
@@ -191,8 +234,11 @@ def test_config4_mixed_batch_sampled():
     q64 = qt.to(torch.float64).cpu().numpy()
     k64n = kt.to(torch.float64).cpu().numpy()
     v64n = vt.to(torch.float64).cpu().numpy()
-    # sampled decode rows: shortest, longest and a spread
-    picks = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 0, 37, 128, 200, 255})
+    # sampled decode rows: 32 rows spread over the context lengths (the
+    # shortest, the longest and evenly spaced ranks between)
+    by_len = np.argsort(ctx, kind="stable")
+    picks = sorted({int(by_len[r]) for r in np.linspace(0, len(ctx) - 1, 32).round().astype(int)})
+    assert len(picks) == 32
     for i in picks:
         L = int(ctx[i])
         keys = np.concatenate([_gen(w.seed * 100000 + 2 * i, (L, G, D)).to(torch.float64).cpu().numpy(),
@@ -208,8 +254,8 @@ def test_config4_mixed_batch_sampled():
     vp = _gen(w.seed * 100000 + 2 * 256 + 1, (pf_cached, G, D)).to(torch.float64).cpu().numpy()
     keys = np.concatenate([kp, k64n[256:]])
     vals = np.concatenate([vp, v64n[256:]])
-    rows = np.array([0, 1, 63, 64, 500, 1023, 1791])
-    for h in range(0, H, 3):
+    rows = np.array([0, 1, 31, 32, 63, 64, 127, 128, 500, 777, 1023, 1024, 1400, 1663, 1790, 1791])
+    for h in range(H):
         g = h // (H // G)
         ref = oa.attention_rows(q64[256 + rows, h], keys[:, g], vals[:, g], pf_cached + rows, w.scale)
         assert_close(got[256 + rows, h], ref, "bf16", f"c4 prefill head {h}")
@@ -249,9 +295,10 @@ def test_config5_long_prompt_sampled_and_monolithic():
     # sampled rows against the oracle, at every chunk
     got = chunked.to(torch.float64).numpy()
     for c0 in range(0, P, 2048):
-        rows = c0 + np.array([0, 777, 2047])
+        rows = c0 + np.array([0, 1, 31, 32, 63, 64, 255, 256, 777, 1023, 1024, 1500, 1983, 2000,
+                              2046, 2047])
         q64 = qt[rows].to(torch.float64).numpy()
-        for h in (0, 7, 8, 33, 63):
+        for h in (0, 7, 8, 17, 26, 33, 42, 51, 60, 63):
             g = h // (H // G)
             ref = oa.attention_rows(q64[:, h], k64[:, g], v64[:, g], rows, w.scale)
             assert_close(got[rows, h], ref, "bf16", f"c5 rows {rows.tolist()} head {h}")

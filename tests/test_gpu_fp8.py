@@ -165,3 +165,54 @@ def test_fp8_codes_of_edge_values():
     gk, gv = pools.canonical()
     want = of8.quantize(k64.reshape(-1), 1.0)
     assert np.array_equal(gk[1, 1, 0], want) and np.array_equal(gv[1, 1, 0], want)
+
+
+@pytest.mark.parametrize("split", [-1, 512], ids=["unsplit", "split512"])
+def test_fp8_growing_scores_move_the_reference(split):
+    """The climbing-score rows of the bf16 test over an fp8 cache whose K
+    scale is not 1 (it is folded into the softmax scale): a ramp and jumps
+    in both 32-key blocks of the tiles move the running reference many
+    times, through the same rescale code as a bf16 cache."""
+    need_gpu()
+    H, G, D, bs, S = 32, 8, 128, 16, 512
+    ks, vs = 0.25, 0.02                    # codes of K up to ~300, of V up to ~250: no saturation
+    rng = np.random.default_rng(12)
+    computed, n = 2000, 600
+    L = computed + n
+    u = rng.standard_normal((G, D))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    jumps = [64 * m + r for m, r in ((4, 5), (11, 40), (17, 55), (23, 20), (32, 60), (37, 35))]
+    ramp = 0.01 * np.arange(L) + 8.0 * np.searchsorted(jumps, np.arange(L), side="right")
+    k = 0.5 * rng.standard_normal((L, G, D)) + ramp[:, None, None] * u[None]
+    kt, k64 = quantize(k, "bf16")
+    vt, v64 = quantize(rng.standard_normal((L, G, D)), "bf16")
+    nb = -(-L // bs) + 20
+    pair = Pair(nb, G, bs, 64, "bf16", 4096, -(-L // bs) + 1, rng.permutation(nb).astype(np.int32))
+    pools = Fp8Pools(nb, G, bs, D)
+    pair.add_partial(0, L, computed)
+    slots = pair.prod.slots(0, 0, computed)
+    fill = {"cu_seqlens_q": np.array([0, computed], np.int32), "cached_seq_len": np.array([0], np.int32),
+            "block_table": np.zeros((1, 1), np.int32), "slot_mapping": slots}
+    pools.call(fill, None, kt[:computed].to(DEV), vt[:computed].to(DEV), 0, ks, vs).reshape_and_cache()
+    pools.oracle_write([pair.orc._find(0).blocks], [0, computed], [0], k64[:computed], v64[:computed],
+                       ks, vs)
+    pb, ob = pair.step()
+    alpha = rng.uniform(8.0, 14.0, H)
+    q = 0.3 * rng.standard_normal((n, H, D)) + alpha[None, :, None] * u[np.arange(H) // (H // G)][None]
+    qt, q64 = quantize(q, "bf16")
+    say(f"fp8 growing scores split={split}")
+    qd = qt.to(DEV)
+    out = torch.full_like(qd, float("nan"))
+    call = pools.call(pb, qd, kt[computed:].to(DEV), vt[computed:].to(DEV), S, ks, vs, out=out,
+                      split_keys_prefill=split)
+    call.set_workspace(torch.empty(max(256, call.workspace_bytes()), dtype=torch.uint8, device=DEV))
+    call()
+    torch.cuda.synchronize()
+    pools.oracle_write(ob["block_table"], ob["cu_seqlens_q"], ob["cached_seq_len"], k64[computed:],
+                       v64[computed:], ks, vs)
+    gk, gv = pools.canonical()
+    assert np.array_equal(gk, pools.ok) and np.array_equal(gv, pools.ov)
+    ref = oa.attention(q64, of8.dequantize(pools.ok, ks), of8.dequantize(pools.ov, vs),
+                       ob["block_table"], ob["cu_seqlens_q"], ob["cached_seq_len"], bs,
+                       1 / math.sqrt(D), G)
+    assert_close(out.to(torch.float64).cpu().numpy(), ref, "bf16", f"fp8 growing/{split}")

@@ -40,7 +40,7 @@ def _resolve(v, S):
     return {"S": S, "2S": 2 * S}.get(v, v)
 
 
-def run_case(case, split, fill=0.0, seed=0, derive_slots=False, inline_desc=False):
+def run_case(case, split, fill=0.0, seed=0, derive_slots=False, inline_desc=False, scale=None):
     name, dtype, H, G, D, bs, S, reqs, decodes, budget = case
     rng = np.random.default_rng(1000 + seed)
     max_blocks = max(-(-(p + 1) // bs) for p, _ in reqs + [(c + 1, 0) for c in decodes]) + 1
@@ -71,9 +71,10 @@ def run_case(case, split, fill=0.0, seed=0, derive_slots=False, inline_desc=Fals
     vt, v64 = quantize(rng.standard_normal((T, G, D)), dtype)
     sp, sd = (_resolve(x, S) for x in SPLITS[split])
     say(f"case {name} split={split} T={T} seqs={pb['num_seqs']}")
-    out, _ = gpu_call(pair.cache, pb, qt, kt, vt, S, split_pre=sp, split_dec=sd,
+    scale = 1 / math.sqrt(D) if scale is None else scale
+    out, _ = gpu_call(pair.cache, pb, qt, kt, vt, S, split_pre=sp, split_dec=sd, scale=scale,
                       derive_slots=derive_slots, inline_desc=inline_desc, attention_twice=inline_desc)
-    ref = pair.oracle_batch(ob, q64, k64, v64, 1 / math.sqrt(D), G)
+    ref = pair.oracle_batch(ob, q64, k64, v64, scale, G)
     return pair, out, ref, dtype
 
 
@@ -116,6 +117,19 @@ def test_inline_descriptor_matches_oracle(case, split):
     gk, gv = pair.cache.canonical_bits()
     assert np.array_equal(gk, bits_of(pair.k_pool, dtype))
     assert np.array_equal(gv, bits_of(pair.v_pool, dtype))
+
+
+@pytest.mark.parametrize("split", ["auto", "seg"])
+@pytest.mark.parametrize("case", [CASES[1], CASES[4], CASES[7], CASES[9]],
+                         ids=["ragged", "bs128", "decodes", "hpg3_bs64"])
+def test_peaked_softmax_stress(case, split):
+    """Q, K ~ N(0, 1) with softmax scale 1: logits have a spread of about
+    sqrt(D) = 11, so a row's weight sits on a few keys and the running
+    maximum moves often; the output stays within the bf16 tolerance."""
+    need_gpu()
+    pair, out, ref, dtype = run_case(case, split, scale=1.0)
+    err = assert_close(out.to(torch.float64).numpy(), ref, dtype, f"{case[0]}/{split}/scale 1")
+    say(f"stress {case[0]}/{split}: max-abs {err[0]:.3g} mean-abs {err[1]:.3g}")
 
 
 @pytest.mark.parametrize("case", [CASES[1], CASES[7], CASES[6]], ids=["ragged", "decodes", "fp32"])
@@ -178,10 +192,11 @@ def test_selector_queries_select_exact_value_rows():
 @pytest.mark.parametrize("split", [-1, 512], ids=["unsplit", "split512"])
 def test_growing_scores_move_the_reference(split):
     """Scores that climb along the keys, by a slow ramp and by jumps placed at
-    key offsets 5, 20, 35, 40, 55 and 60 of their 64-key tiles (each of the
-    first 32, the next 16 and the last 16 keys of a tile), so that the
-    running reference of the online softmax moves many times per row and at
-    every point of a tile where the kernel may move it."""
+    key offsets 5, 20, 35, 40, 55 and 60 of their 64-key tiles (both 32-key
+    blocks, whose exp sums the kernel checks one block at a time, with jumps
+    in each 16-key half of them), so that the running reference of the
+    online softmax moves many times per row and in every block where the
+    kernel may move it."""
     need_gpu()
     H, G, D, bs, S = 32, 8, 128, 16, 512
     rng = np.random.default_rng(11)

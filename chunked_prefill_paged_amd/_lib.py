@@ -85,6 +85,7 @@ SIGNATURES = {
     "cpa_attention": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _vp]),
     "cpa_attention_timed": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _vp, _vp, _vp]),
     "cpa_chunked_prefill_attn": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _vp]),
+    "cpa_chunked_prefill_attn_noalloc": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _vp]),
     "cpa_rope_reshape_and_cache": (ctypes.c_int, [ctypes.POINTER(AttnArgs), ctypes.POINTER(RopeArgs), _vp]),
     "cpa_rope_prepare": (ctypes.c_int, [ctypes.POINTER(AttnArgs), ctypes.POINTER(RopeArgs), _vp]),
     "cpa_rope_chunked_prefill_attn": (ctypes.c_int, [ctypes.POINTER(AttnArgs), ctypes.POINTER(RopeArgs), _vp]),

@@ -161,6 +161,13 @@ class AttnCall:
         _lib.check(_lib.lib().cpa_chunked_prefill_attn(ctypes.byref(self.args), _stream(stream)),
                    "cpa_chunked_prefill_attn")
 
+    def call_noalloc(self, stream=None) -> None:
+        """The whole chunk step on the library's own per-GPU scratch (the
+        workspace set here is not used)."""
+        _lib.check(_lib.lib().cpa_chunked_prefill_attn_noalloc(ctypes.byref(self.args),
+                                                               _stream(stream)),
+                   "cpa_chunked_prefill_attn_noalloc")
+
     # rotary position embedding fused into the cache write (``rope`` is a
     # ``Rope``); the rotated queries land in ``rope.q_out``
     def rope_reshape_and_cache(self, rope, stream=None) -> None:

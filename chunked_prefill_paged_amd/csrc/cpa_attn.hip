@@ -44,6 +44,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "chunked_prefill_attn.h"
 #include "cpa_plan.h"
@@ -1704,6 +1705,14 @@ cpa_status launch_attention(const cpa_attn_args* a, const Resolved* r, hipStream
     return CPA_OK;
 }
 
+// Scratch of the entry point that allocates nothing: one array per GPU,
+// held from the code object's load to the end of the process.  In host code
+// `scratch` names a host-side stand-in; the device address of each GPU's
+// copy comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is ever handed to a launch.
+constexpr size_t kNoAllocScratch = CPA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kNoAllocScratch];
+
 }  // namespace cpa
 
 using namespace cpa;
@@ -1749,6 +1758,24 @@ cpa_status attn_dispatch(const cpa_attn_args* a, const Resolved* r, hipStream_t 
 
 cpa_status check_workspace(const cpa_attn_args* a, const Resolved* r) {
     if (!a->workspace || a->workspace_bytes < r->ws.total) return CPA_ERR_WORKSPACE;
+    return CPA_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+cpa_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return CPA_ERR_HIP;
+    if (dev >= kMaxDevices) return CPA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return CPA_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return CPA_OK;
 }
 
@@ -1845,6 +1872,22 @@ cpa_status cpa_chunked_prefill_attn(const cpa_attn_args* a, void* stream) {
     cpa_status st = cpa_prepare(a, stream);
     if (st != CPA_OK) return st;
     return cpa_attention(a, stream);
+}
+
+cpa_status cpa_chunked_prefill_attn_noalloc(const cpa_attn_args* a, void* stream) {
+    Resolved r;
+    cpa_status st = resolve(a, &r);
+    if (st != CPA_OK) return st;
+    if (r.ws.total > kNoAllocScratch) return CPA_ERR_WORKSPACE;
+    void* ptr = nullptr;
+    if ((st = scratch_address(&ptr)) != CPA_OK) return st;
+    // the prepare launch writes every scratch byte the attention launch
+    // reads (plan, descriptor copy; partials before their merge), so
+    // nothing needs clearing
+    cpa_attn_args local = *a;
+    local.workspace = ptr;
+    local.workspace_bytes = kNoAllocScratch;
+    return cpa_chunked_prefill_attn(&local, stream);
 }
 
 cpa_status cpa_rope_reshape_and_cache(const cpa_attn_args* a, const cpa_rope_args* rope, void* stream) {

@@ -202,6 +202,22 @@ cpa_status cpa_attention_timed(const cpa_attn_args* args, void* stream, void* st
 /* cpa_prepare followed by cpa_attention: the whole chunk step. */
 cpa_status cpa_chunked_prefill_attn(const cpa_attn_args* args, void* stream);
 
+/* Bytes of the library's own per-GPU scratch (below). */
+#define CPA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* cpa_chunked_prefill_attn for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * plan and any partial states go to a scratch array of
+ * CPA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU from its
+ * first use there until the process ends; args->workspace and
+ * args->workspace_bytes are ignored.  No allocation or free of any kind
+ * happens in the call.  Every call on one GPU shares that GPU's scratch, so
+ * calls that overlap on one GPU (other streams, other threads) race: the
+ * caller serialises them.  CPA_ERR_WORKSPACE when the call needs more than
+ * CPA_NOALLOC_SCRATCH_BYTES (cpa_workspace_bytes tells); otherwise as
+ * cpa_chunked_prefill_attn. */
+cpa_status cpa_chunked_prefill_attn_noalloc(const cpa_attn_args* args, void* stream);
+
 /* ---------------------------------------------------------------------
  * Rotary position embedding fused into the cache write.
  *

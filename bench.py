@@ -59,10 +59,15 @@ def _args():
     ap.add_argument("--event-timing", choices=("dispatch", "records"), default="dispatch",
                     help="per-launch attention timing: events taken by the kernel's own dispatch "
                          "(cpa_attention_timed), or event records around the launch")
-    ap.add_argument("--workload", choices=("c2", "c4", "c5", "rope"), default="c2",
-                    help="c2: the 10k prompt (headline line); c5: the 32k prompt, per chunk "
-                         "and against one monolithic call; c4: the mixed decode + prefill batch; "
-                         "rope: the cache write with rotary embedding fused in, at two chunk shapes")
+    ap.add_argument("--workload", choices=("c2", "c2tp", "c3", "c4", "c5", "rope"), default="c2",
+                    help="c2: the 10k prompt (headline line); c2tp: the 10k prompt at one "
+                         "tensor-parallel share of eight (H4/G1); c3: 16 prefix-cached requests "
+                         "in one varlen call; c5: the 32k prompt, per chunk and against one "
+                         "monolithic call; c4: the mixed decode + prefill batch; rope: the cache "
+                         "write with rotary embedding fused in, at two chunk shapes")
+    ap.add_argument("--steady-warmup", type=int, default=100,
+                    help="after the timed steps, this many more untimed steps, then the same "
+                         "number of timed steps again: the steady-state rate (0: skip)")
     ap.add_argument("--kv-cache", choices=("bf16", "fp8"), default="bf16",
                     help="KV cache element type for c2/c5/c4: bf16, or E4M3 codes under per-tensor "
                          "scales (attention still computes in bf16)")
@@ -132,7 +137,7 @@ class PromptBench:
         from synth import free_block_order, get_workload, prompt_qkv
 
         self.torch = torch
-        w = get_workload(workload)
+        w = get_workload(workload) if isinstance(workload, str) else workload
         self.w = w
         q32, k32, v32 = prompt_qkv(w)
         dev = "cuda"
@@ -306,9 +311,31 @@ def cpu_baseline(w, max_blocks):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": round(elapsed, 2),
+            "host_cpus": os.cpu_count(), "cpus_available": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model(),
             "sample": f"{steps} whole steps: the 10k prompt's 5 chunks (2048x4 + 1808), all 32 "
                       "query heads, oracle scheduler + cache write + attention in numpy float64 "
                       f"({flops / 1e9:.2f} GFLOP)"}
+
+
+def cpu_model() -> str:
+    """Model name of the host CPU (as lscpu reports it)."""
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _time_steps(torch, fn, steps, warmup):
@@ -578,11 +605,15 @@ def main():
     if args.workload == "rope":
         run_rope(args)
         return
-    bench = PromptBench(args.kv_segment_size, args.split_keys_prefill, kv_fp8=args.kv_cache == "fp8")
-    flops = bench.flops_per_step()
-    for _ in range(args.warmup):
-        bench.step()
-    torch.cuda.synchronize()
+    if args.workload == "c3":
+        run_prefix_batch(args)
+        return
+    run_prompt(args)
+
+
+def _timed_steps(torch, args, bench):
+    """K timed steps with the per-launch attention events; returns (wall
+    seconds, attention ms summed over launches, mean ms per chunk)."""
     if args.event_timing == "dispatch":
         hip = HipEvents()
         events = [[(hip.create(), hip.create()) for _ in bench.chunks] for _ in range(args.steps)]
@@ -606,9 +637,29 @@ def main():
             for a, b in step:
                 hip.destroy(a)
                 hip.destroy(b)
+    return elapsed, attn_ms, per_chunk_ms
+
+
+def run_prompt(args):
+    """The 10k prompt (the headline line), or its tensor-parallel share."""
+    import dataclasses
+
+    import torch
+    from synth import get_workload
+    w = get_workload("c2")
+    tp = args.workload == "c2tp"
+    if tp:   # one GPU's share of an eight-way split by KV-head group
+        w = dataclasses.replace(w, num_heads=w.num_heads // w.num_kv_heads, num_kv_heads=1)
+    bench = PromptBench(args.kv_segment_size, args.split_keys_prefill, workload=w,
+                        kv_fp8=args.kv_cache == "fp8")
+    flops = bench.flops_per_step()
+    for _ in range(args.warmup):
+        bench.step()
+    torch.cuda.synchronize()
+    elapsed, attn_ms, per_chunk_ms = _timed_steps(torch, args, bench)
     value = flops * args.steps / elapsed / 1e12
     achieved = flops * args.steps / (attn_ms / 1e3) / 1e12
-    w = bench.w
+    shape = f"H{w.num_heads}/G{w.num_kv_heads}/D{w.head_dim}"
     line = {
         "metric": "chunked-prefill attention TFLOP/s + % of bf16 MFMA peak (10k GQA prompt)",
         "value": round(value, 2),
@@ -623,8 +674,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "10k-token GQA chunked prefill: chunks 2048x4+1808 (cached 0..8192), "
-                        f"H32/G8/D128, block_size 128, kv_segment_size {args.kv_segment_size}",
+            "workload": ("10k-token GQA chunked prefill: chunks 2048x4+1808 (cached 0..8192), "
+                         f"{shape}, block_size 128, kv_segment_size {args.kv_segment_size}"
+                         + (", one KV-head group of eight (tensor-parallel share)" if tp else "")),
             "global_batch": 1, "seq_len": w.prompt_len, "parallelism": "none (1 GPU)",
             "kv_cache": args.kv_cache,
         },
@@ -633,17 +685,106 @@ def main():
         "attention_ms_per_chunk": [round(x, 4) for x in per_chunk_ms],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": recorded_traffic() if args.kv_cache == "bf16" else None,
-                     "kernel": "attn_kernel<bf16,128> (+ merge_kernel when rows are split)",
+                     "traffic": recorded_traffic() if args.kv_cache == "bf16" and not tp else None,
+                     "kernel": "attn_kernel<bf16,128>",
                      "timing": ("HIP events taken by the attention kernel's dispatch "
-                                "(hipExtLaunchKernel), every launch of the timed steps"
+                                "(hipExtLaunchKernel), every launch of the timed steps; the merge "
+                                "launch of split rows follows them"
                                 if args.event_timing == "dispatch" else
-                                "HIP event records around every attention launch of the timed steps")},
+                                "HIP event records around every attention call of the timed steps")},
         "plan": [{"items": p["num_items"], "merge_rows": p["num_merge_rows"]} for p in bench.plan],
     }
-    if not args.no_cpu_baseline and args.kv_cache == "bf16":
+    if args.steady_warmup > 0:
+        # the same measurement again after more untimed steps: the first
+        # steps of a process run below the rate the GPU settles at
+        for _ in range(args.steady_warmup):
+            bench.step()
+        torch.cuda.synchronize()
+        el2, attn2, chunks2 = _timed_steps(torch, args, bench)
+        line["steady_state"] = {
+            "untimed_steps_before": args.warmup + args.steps + args.steady_warmup,
+            "value": round(flops * args.steps / el2 / 1e12, 2),
+            "ms_per_step": round(el2 * 1e3 / args.steps, 4),
+            "roofline_achieved": round(flops * args.steps / (attn2 / 1e3) / 1e12, 2),
+            "attention_ms_per_chunk": [round(x, 4) for x in chunks2],
+        }
+    if not args.no_cpu_baseline and args.kv_cache == "bf16" and not tp:
         line["cpu_baseline"] = cpu_baseline(bench.w, bench.max_blocks)
     print(json.dumps(line), flush=True)
+
+
+def run_prefix_batch(args):
+    """Config 3: 16 requests share a 4096-token prefix held in 256 blocks
+    (block size 16, reference counted); one varlen call computes their
+    suffixes (16*U{16..32} tokens each) at cached_seq_len 4096: the cache
+    write of the suffixes and the attention.  TFLOP/s over the algorithmic
+    FLOPs of the call."""
+    import torch
+    from chunked_prefill_paged_amd import AttnCall, HostScheduler, cache_shapes
+    from synth import config3_suffix_lengths, free_block_order, get_workload
+
+    w = get_workload("c3")
+    H, G, D, bs = w.num_heads, w.num_kv_heads, w.head_dim, w.block_size
+    prefix = w.prompt_len
+    suffix = [int(x) for x in config3_suffix_lengths(w)]
+    nb = prefix // bs + sum(-(-x // bs) for x in suffix) + 64
+    sched = HostScheduler(nb, bs, w.max_batched_tokens, -(-(prefix + 512) // bs),
+                          free_order=free_block_order(nb, w.seed))
+    sched.add_decode(999, prefix)                 # the request that computed the prefix
+    shared = list(sched.request_blocks(999))
+    for i, x in enumerate(suffix):
+        sched.add_request(i, prefix + x, shared)
+    sched.free_request(999)
+    b = sched.step()
+    T = int(b["num_tokens"])
+    dev = "cuda"
+    ks, vs = cache_shapes(nb, G, bs, D)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    k_cache = torch.randn(ks, generator=gen, device=dev).to(torch.bfloat16)
+    v_cache = torch.randn(vs, generator=gen, device=dev).to(torch.bfloat16)
+    q = torch.randn((T, H, D), generator=gen, device=dev).to(torch.bfloat16)
+    kn = torch.randn((T, G, D), generator=gen, device=dev).to(torch.bfloat16)
+    vn = torch.randn((T, G, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    d = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)   # noqa: E731
+    call = AttnCall(q=q, k_new=kn, v_new=vn, k_cache=k_cache, v_cache=v_cache, out=out,
+                    cu_seqlens_q=d(b["cu_seqlens_q"], np.int32),
+                    cached_seq_len=d(b["cached_seq_len"], np.int32),
+                    block_table=d(b["block_table"], np.int32), slot_mapping=None,
+                    h_cu_seqlens_q=np.asarray(b["cu_seqlens_q"], np.int32),
+                    h_cached_seq_len=np.asarray(b["cached_seq_len"], np.int32),
+                    kv_segment_size=w.kv_segment_size, split_keys_prefill=args.split_keys_prefill)
+    call.set_workspace(torch.empty(max(256, call.workspace_bytes()), dtype=torch.uint8, device=dev))
+    flops = sum(4 * H * D * (x * prefix + x * (x + 1) // 2) for x in suffix)
+    steps, warm = max(1, args.steps), max(1, args.warmup)
+    t = _time_steps(torch, call, steps, warm)
+    hip = HipEvents()
+    evs = [(hip.create(), hip.create()) for _ in range(steps)]
+    for a, e in evs:
+        call.prepare()
+        call.attention_timed(a, e)
+    torch.cuda.synchronize()
+    kern_ms = sum(hip.elapsed_ms(a, e) for a, e in evs) / steps
+    for a, e in evs:
+        hip.destroy(a)
+        hip.destroy(e)
+    value = flops / t / 1e12
+    print(json.dumps({
+        "metric": "prefix-cached batch: attention TFLOP/s over the suffixes (config 3)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(t * 1e3, 4), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"16 requests x suffix 16*U{{16..32}} ({T} tokens) over a shared "
+                               f"4096-token prefix in 256 blocks, bs16, S{w.kv_segment_size}, "
+                               f"H{H}/G{G}/D{D}"},
+        "gflop_per_step": round(flops / 1e9, 2),
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(flops / (kern_ms / 1e3) / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (kern_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_kernel<bf16,128>"},
+    }), flush=True)
 
 
 if __name__ == "__main__":

@@ -126,6 +126,19 @@ def test_cache_write_refuses_bad_host_mirrors(over):
     assert _lib.lib().cpa_rope_reshape_and_cache(ctypes.byref(a), p, None) == _lib.CPA_ERR_INVALID_ARG
 
 
+def test_no_alloc_call_refuses_more_than_its_scratch():
+    # 8 decode rows over a million cached tokens each, split per 512-key
+    # segment: ~1954 partial states per (row, head), about 260 MB > 64 MiB.
+    # Refused from the host-side plan alone, before any device call.
+    cu = np.arange(9, dtype=np.int32)
+    cached = np.full(8, 1_000_000, dtype=np.int32)
+    a, _keep = _args(num_seqs=8, total_q=8, cu=cu, cached=cached, max_blocks_per_seq=62501,
+                     num_blocks=600000, kv_segment_size=512, split_keys_decode=512)
+    st, info = _plan(a)
+    assert st == 0 and info.workspace_bytes > (64 << 20)
+    assert _lib.lib().cpa_chunked_prefill_attn_noalloc(ctypes.byref(a), None) == _lib.CPA_ERR_WORKSPACE
+
+
 def test_missing_workspace_is_refused_before_launch():
     a, _keep = _args()
     a.workspace, a.workspace_bytes = 0, 0

@@ -27,6 +27,7 @@ it is reported only while those sources are unchanged (null otherwise).
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -339,6 +340,8 @@ def cpu_model() -> str:
 
 
 def _time_steps(torch, fn, steps, warmup):
+    gc.collect()
+    gc.disable()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -346,6 +349,7 @@ def _time_steps(torch, fn, steps, warmup):
     for _ in range(steps):
         fn()
     torch.cuda.synchronize()
+    gc.enable()
     return (time.perf_counter() - t0) / steps
 
 
@@ -611,6 +615,36 @@ def main():
     run_prompt(args)
 
 
+class RunAhead:
+    """Keeps the host at most `depth` steps ahead of the GPU: before a step
+    is enqueued, the event recorded at the end of the step `depth` back is
+    awaited.  A serving loop cannot run further ahead than its outputs allow;
+    without a bound the host here enqueues dozens of steps ahead, and the
+    runtime's one-time growth of its launch resources then stalls the host
+    for ~30 ms with the GPU idle (and its clock falling back)."""
+
+    def __init__(self, torch, depth=2):
+        self.torch, self.depth, self.marks = torch, depth, []
+
+    def before(self):
+        if len(self.marks) >= self.depth:
+            self.marks.pop(0).synchronize()
+
+    def after(self):
+        ev = self.torch.cuda.Event()
+        ev.record()
+        self.marks.append(ev)
+
+
+def _steps(torch, bench, n):
+    """n untimed steps under the run-ahead bound."""
+    ra = RunAhead(torch)
+    for _ in range(n):
+        ra.before()
+        bench.step()
+        ra.after()
+
+
 def _timed_steps(torch, args, bench):
     """K timed steps with the per-launch attention events; returns (wall
     seconds, attention ms summed over launches, mean ms per chunk)."""
@@ -623,10 +657,13 @@ def _timed_steps(torch, args, bench):
                    for _ in bench.chunks] for _ in range(args.steps)]
         elapsed_ms = lambda a, b: a.elapsed_time(b)   # noqa: E731
     torch.cuda.synchronize()
+    ra = RunAhead(torch)
     t0 = time.perf_counter()
     for s in range(args.steps):
         ev = [list(p) for p in events[s]]
+        ra.before()
         bench.step(ev)
+        ra.after()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     attn_ms = sum(elapsed_ms(a, b) for step in events for (a, b) in step)
@@ -653,8 +690,12 @@ def run_prompt(args):
     bench = PromptBench(args.kv_segment_size, args.split_keys_prefill, workload=w,
                         kv_fp8=args.kv_cache == "fp8")
     flops = bench.flops_per_step()
-    for _ in range(args.warmup):
-        bench.step()
+    # no collector pauses in the loops: a full collection over torch's heap
+    # stalls the host ~30 ms, with the GPU idle, at an unpredictable step
+    gc.collect()
+    gc.freeze()
+    gc.disable()
+    _steps(torch, bench, args.warmup)
     torch.cuda.synchronize()
     elapsed, attn_ms, per_chunk_ms = _timed_steps(torch, args, bench)
     value = flops * args.steps / elapsed / 1e12
@@ -697,8 +738,7 @@ def run_prompt(args):
     if args.steady_warmup > 0:
         # the same measurement again after more untimed steps: the first
         # steps of a process run below the rate the GPU settles at
-        for _ in range(args.steady_warmup):
-            bench.step()
+        _steps(torch, bench, args.steady_warmup)
         torch.cuda.synchronize()
         el2, attn2, chunks2 = _timed_steps(torch, args, bench)
         line["steady_state"] = {
@@ -708,6 +748,7 @@ def run_prompt(args):
             "roofline_achieved": round(flops * args.steps / (attn2 / 1e3) / 1e12, 2),
             "attention_ms_per_chunk": [round(x, 4) for x in chunks2],
         }
+    gc.enable()
     if not args.no_cpu_baseline and args.kv_cache == "bf16" and not tp:
         line["cpu_baseline"] = cpu_baseline(bench.w, bench.max_blocks)
     print(json.dumps(line), flush=True)

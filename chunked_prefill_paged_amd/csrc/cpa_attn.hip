@@ -1202,6 +1202,7 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
     }
     __syncthreads();
     // V columns: kCacheTok lanes over tokens, the rest of the wave over d
+    // (a 16-byte store of 8 consecutive tokens per lane measured no faster)
     constexpr int kLanesD = 64 / kCacheTok;
     const int lane = tid & 63, wave = tid >> 6;
     const int tk = lane % kCacheTok;
@@ -1451,6 +1452,9 @@ cpa_status check_common(const cpa_attn_args* a) {
     return CPA_OK;
 }
 
+// Workgroups that fill MI355X in one pass: 256 CUs x 2 resident workgroups.
+constexpr int64_t kFillWgs = 512;
+
 cpa_status resolve(const cpa_attn_args* a, Resolved* r) {
     cpa_status st = check_common(a);
     if (st != CPA_OK) return st;
@@ -1480,7 +1484,6 @@ cpa_status resolve(const cpa_attn_args* a, Resolved* r) {
     const int32_t* cu = a->h_cu_seqlens_q;
     const int32_t* cc = a->h_cached_seq_len;
     if (cu[0] != 0 || cu[a->num_seqs] != a->total_q) return CPA_ERR_INVALID_ARG;
-    int64_t items = 0, parts = 0, merge = 0;
     for (int b = 0; b < a->num_seqs; ++b) {
         const int64_t n = (int64_t)cu[b + 1] - cu[b];
         if (n < 0 || cc[b] < 0) return CPA_ERR_INVALID_ARG;
@@ -1488,11 +1491,31 @@ cpa_status resolve(const cpa_attn_args* a, Resolved* r) {
         const int64_t kv = cc[b] + n;
         if (kv >= ((int64_t)1 << 30)) return CPA_ERR_INVALID_ARG;
         if ((kv + a->block_size - 1) / a->block_size > a->max_blocks_per_seq) return CPA_ERR_INVALID_ARG;
-        const SeqPlan sp = seq_plan((int32_t)n, cc[b], r->hpg, a->num_heads, r->dec_thresh, r->split_pre,
-                                    r->split_dec);
-        items += sp.items;
-        parts += sp.parts;
-        merge += sp.merge;
+    }
+    int64_t items = 0, parts = 0, merge = 0;
+    auto count = [&](int32_t split_pre) {
+        items = parts = merge = 0;
+        for (int b = 0; b < a->num_seqs; ++b) {
+            const SeqPlan sp = seq_plan(cu[b + 1] - cu[b], cc[b], r->hpg, a->num_heads, r->dec_thresh,
+                                        split_pre, r->split_dec);
+            items += sp.items;
+            parts += sp.parts;
+            merge += sp.merge;
+        }
+    };
+    count(r->split_pre);
+    // Automatic prefill splits: when the call's work items leave most of the
+    // GPU idle (fewer workgroups than half of kFillWgs, one per CU; e.g. one
+    // KV-head group's share of a prompt), prefill rows are split into key
+    // ranges of 8, 4, 2 or 1 segments, the longest that fills the GPU, their
+    // partial states merged afterwards.  (A grid close to kFillWgs is left
+    // alone: splitting it only adds a second pass and the merge.)
+    if (a->split_keys_prefill == 0 && 2 * items * a->num_kv_heads < kFillWgs) {
+        for (int mult : {8, 4, 2, 1}) {
+            count(seg * mult);
+            r->split_pre = seg * mult;
+            if (items * a->num_kv_heads >= kFillWgs) break;
+        }
     }
     if (items * a->num_kv_heads >= ((int64_t)1 << 31) || parts >= ((int64_t)1 << 31)) return CPA_ERR_UNSUPPORTED;
     r->items = items;

@@ -102,7 +102,13 @@ typedef struct cpa_attn_args {
                                        0 means 1 ("1 + max_num_draft_tokens")   */
     int32_t split_keys_prefill;     /* keys per work item for prefill rows:
                                        0 automatic, -1 never split, else a
-                                       multiple of kv_segment_size              */
+                                       multiple of kv_segment_size.  Automatic
+                                       leaves rows unsplit unless the call's
+                                       work items times num_kv_heads number
+                                       under 256 (one per CU of MI355X); then
+                                       it takes the longest of 8, 4, 2, 1
+                                       segments per item that reaches 512 (one
+                                       full pass), or 1 segment                 */
     int32_t split_keys_decode;      /* same for decode rows (0: one segment)    */
     float   scale;                  /* softmax scale > 0, usually 1/sqrt(D)     */
     const void* q;                  /* device                                   */

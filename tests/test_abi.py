@@ -73,8 +73,15 @@ def test_plan_counts_for_a_valid_batch():
     a, _keep = _args()
     st, info = _plan(a)
     assert st == 0
-    # seq 0: 100 tokens x 4 heads = 400 rows -> 4 tiles; seq 1: 200 x 4 = 800 -> 7 tiles
-    assert info.num_items == 4 + 7 and info.num_merge_rows == 0 and info.num_partials == 0
+    # seq 0: 100 tokens x 4 heads = 400 rows -> 4 tiles; seq 1: 200 x 4 = 800 -> 7 tiles.
+    # 11 items x 8 KV heads = 88 workgroups leave the GPU idle, so the
+    # automatic plan splits prefill rows at the smallest step tried, one
+    # segment (1024 keys): seq 0 (kv 1100) -> 2 splits, seq 1 (kv 200) -> 1
+    assert info.num_items == 4 * 2 + 7 and info.num_merge_rows == 100
+    assert info.num_partials == 2 * 100 * 32 and info.split_keys_prefill == 1024
+    a0, _k0 = _args(split_keys_prefill=-1)
+    st, info = _plan(a0)
+    assert st == 0 and info.num_items == 4 + 7 and info.num_merge_rows == 0 and info.num_partials == 0
     a2, _k2 = _args(split_keys_prefill=1024)
     st, info = _plan(a2)
     # seq 0 kv 1100 -> 2 splits; seq 1 kv 200 -> 1

@@ -59,6 +59,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kKeys = 64;   // keys per LDS tile
 constexpr int kXcds = 8;
+// Attention workgroups resident on one XCD at a time (32 CUs x 2).  The
+// dispatcher hands an XCD's first such workgroups out across its CUs, CU j
+// taking the j-th and the (j + 32)-th.
+constexpr int kPairSlots = 64;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // ---------------------------------------------------------------------------
@@ -1282,7 +1286,12 @@ __device__ V block_scan_incl(V x, V* buf) {
 // in sequence order, each sequence's longest row tiles first; items of
 // decode rows follow.  Long causal items thus start before the short ones,
 // and in a mixed batch the matrix-bound prefill items run while the
-// bandwidth-bound decode items fill the remaining slots.
+// bandwidth-bound decode items fill the remaining slots.  Within the first
+// kPairSlots row tiles of a sequence (the F longest), the lighter half runs
+// in ascending order, so that a CU's two first workgroups are the j-th
+// longest and the j-th shortest of them: the causal triangle's long and
+// short rows share a CU, and the long one has the CU to itself once the
+// short one ends.
 __device__ void build_plan(const PrepParams& p, char* smem) {
     int* s_item = (int*)smem;                 // [kMaxSeqs + 1] first item of the k-th issued sequence
     int* s_merge = s_item + (kMaxSeqs + 1);   // [kMaxSeqs + 1] first merge row of sequence b
@@ -1365,8 +1374,11 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
         const int i0 = s_item[k], ni = s_item[k + 1] - i0;
         const int nsplit = s_nsplit[k];
         const int tiles = ni / nsplit;
+        const int F = min(tiles, kPairSlots);
         for (int local = ln; local < ni; local += 64) {
-            const int rt = tiles - 1 - local / nsplit;   // longest row tiles first
+            const int li = local / nsplit;
+            int rt = tiles - 1 - li;                     // longest row tiles first
+            if (li < F && li >= F - F / 2) rt = tiles - F + (li - (F - F / 2));
             p.items[i0 + local] = make_int4(bq, rt, local % nsplit, nsplit);
         }
     }

@@ -619,12 +619,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     // 32-key block sb) at k_base + ((s8*16) ^ k_x) + sb*32*D*2; V fragment
     // (k-step ks, d tile dt) at v_base + ((ks*32) ^ v_x) + dt*32*64*2.
     uint32_t k_base = 0, k_x = 0, v_base = 0, v_x = 0;
+    // The same offsets summed once per fragment column: K k-step f at
+    // kad[f] (+ 8 KiB for the second 32-key block), V k-step ks at vad[ks]
+    // (+ 4 KiB per d tile).  The empty asm keeps the sums whole: otherwise
+    // the compiler re-adds the two parts before every LDS read, one VALU
+    // instruction each on the issue port the softmax needs.
+    uint32_t kad[8] = {}, vad[4] = {};
     if constexpr (kHandOrdered) {
         k_base = (uint32_t)(swap_bits23(lrow) * D * 2 + ((half * 8) ^ (lane & 8)) * 16);
         k_x = (uint32_t)((lane & 7) * 16);
         const int swl = ((lrow & 7) ^ ((lrow >> 3) & 1)) & SWV;
         v_base = (uint32_t)(lrow * kKeys * 2 + (half ^ (swl & 1)) * 16);
         v_x = (uint32_t)((swl & 6) * 16);
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            kad[f] = k_base + ((f * 16) ^ k_x);
+            asm volatile("" : "+v"(kad[f]));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            vad[ks] = v_base + ((ks * 32) ^ v_x);
+            asm volatile("" : "+v"(vad[ks]));
+        }
     }
     // The hand-ordered path's raw score accumulators (each QK chain starts
     // from zero).  The softmax scale is applied in float to every score, in
@@ -639,10 +655,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             const char* kb = (const char*)&lds_k[buf][0];
             const char* vb = (const char*)&lds_v[buf][0];
             auto kfrag = [&](int f) {
-                return *(const bf16x8*)(kb + (k_base + (((f & 7) * 16) ^ k_x)) + (f >> 3) * (32 * D * 2));
+                return *(const bf16x8*)(kb + kad[f & 7] + (f >> 3) * (32 * D * 2));
             };
             auto vfrag = [&](int i) {
-                return *(const bf16x8*)(vb + (v_base + (((i >> 2) * 32) ^ v_x)) + (i & 3) * (32 * kKeys * 2));
+                return *(const bf16x8*)(vb + vad[i >> 2] + (i & 3) * (32 * kKeys * 2));
             };
             // fragment j of the tile's 32 LDS reads: K fragments 0..15, then V 0..15
             auto frag = [&](int j) { return j < 16 ? kfrag(j) : vfrag(j - 16); };
@@ -810,9 +826,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             if (nfull > 1) btn = load_bt(tstart(1));
         }
         wait_vmem();                     // Q and the first block ids
-        for (int u = 0; u < ntiles; ++u) {
+        // One tile.  The loop below calls it twice per iteration with buf a
+        // constant, so every LDS fragment read is a fixed register plus an
+        // immediate offset, with no address arithmetic in the tile.
+        auto tile = [&](const int u, const int buf) __attribute__((always_inline)) {
             const int ts = tstart(u);
-            const int buf = u & 1;
             if (!FP8 && u >= nfull) {    // the sequence's last tile
                 load_tile_edge(ts);
                 store_tile(buf);
@@ -847,6 +865,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             if constexpr (FP8) {
                 if (u + 1 < ntiles) store_tile_fp8(buf ^ 1);
             }
+        };
+        for (int u = 0; u < ntiles; u += 2) {
+            tile(u, 0);
+            if (u + 1 < ntiles) tile(u + 1, 1);
         }
     }
 

@@ -1287,21 +1287,42 @@ __device__ void rope_queries(const PrepParams& p, int qgrp) {
     }
 }
 
-// Inclusive scan of one value per thread over the workgroup (log-step).
-template <typename V>
-__device__ V block_scan_incl(V x, V* buf) {
-    const int tid = threadIdx.x;
-    buf[tid] = x;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-        const V y = tid >= off ? buf[tid - off] : V(0);
-        __syncthreads();
-        buf[tid] += y;
-        __syncthreads();
+// The plan's per-thread counters, scanned together.
+struct PlanCounts {
+    long long it_pre, it_dec, parts;
+    int merge, n_pre;
+};
+
+// Inclusive scan of the counters over the workgroup: within each wave by
+// shuffles, then the totals of the waves before it through LDS (two
+// barriers; a barrier per step of a shared-memory scan made the plan
+// builder the longest part of the prepare launch).
+__device__ PlanCounts block_scan_incl(PlanCounts x, PlanCounts* wtot) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const long long a = __shfl_up(x.it_pre, off), b = __shfl_up(x.it_dec, off),
+                        c = __shfl_up(x.parts, off);
+        const int d = __shfl_up(x.merge, off), e = __shfl_up(x.n_pre, off);
+        if (lane >= off) {
+            x.it_pre += a;
+            x.it_dec += b;
+            x.parts += c;
+            x.merge += d;
+            x.n_pre += e;
+        }
     }
-    const V r = buf[tid];
+    if (lane == 63) wtot[w] = x;
     __syncthreads();
-    return r;
+    for (int i = 0; i < w; ++i) {
+        x.it_pre += wtot[i].it_pre;
+        x.it_dec += wtot[i].it_dec;
+        x.parts += wtot[i].parts;
+        x.merge += wtot[i].merge;
+        x.n_pre += wtot[i].n_pre;
+    }
+    __syncthreads();
+    return x;
 }
 
 // Work plan.  Items of prefill sequences (n > decode threshold) come first,
@@ -1319,8 +1340,7 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
     int* s_merge = s_item + (kMaxSeqs + 1);   // [kMaxSeqs + 1] first merge row of sequence b
     int* s_nsplit = s_merge + (kMaxSeqs + 1); // [kMaxSeqs]     splits of the k-th issued sequence
     uint16_t* s_seq = (uint16_t*)(s_nsplit + kMaxSeqs);   // [kMaxSeqs] sequence issued k-th
-    __shared__ long long sc_ll[kThreads];
-    __shared__ int sc_i[kThreads];
+    __shared__ PlanCounts sc_w[kThreads / 64];
     const int B = p.num_seqs, tid = threadIdx.x;
     const int per = (B + kThreads - 1) / kThreads;
     const int b_lo = min(B, tid * per), b_hi = min(B, b_lo + per);
@@ -1342,11 +1362,9 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
         parts += sp.parts;
         merge += sp.merge;
     }
-    const long long sc_pre = block_scan_incl(it_pre, sc_ll);
-    const long long sc_dec = block_scan_incl(it_dec, sc_ll);
-    const long long sc_parts = block_scan_incl(parts, sc_ll);
-    const int sc_merge = block_scan_incl(merge, sc_i);
-    const int sc_npre = block_scan_incl(n_pre, sc_i);
+    const PlanCounts sc = block_scan_incl(PlanCounts{it_pre, it_dec, parts, merge, n_pre}, sc_w);
+    const long long sc_pre = sc.it_pre, sc_dec = sc.it_dec, sc_parts = sc.parts;
+    const int sc_merge = sc.merge, sc_npre = sc.n_pre;
     __shared__ long long tot[3];
     __shared__ int tot_i[2];
     if (tid == kThreads - 1) {

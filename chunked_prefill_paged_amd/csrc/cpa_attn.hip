@@ -866,9 +866,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
                 if (u + 1 < ntiles) store_tile_fp8(buf ^ 1);
             }
         };
-        for (int u = 0; u < ntiles; u += 2) {
-            tile(u, 0);
-            if (u + 1 < ntiles) tile(u + 1, 1);
+        if (bs >= kKeys) {
+            for (int u = 0; u < ntiles; u += 2) {
+                tile(u, 0);
+                if (u + 1 < ntiles) tile(u + 1, 1);
+            }
+        } else {
+            // (small blocks: one tile body, the buffer chosen at run time;
+            // two bodies measured slower here)
+            for (int u = 0; u < ntiles; ++u) tile(u, u & 1);
         }
     }
 

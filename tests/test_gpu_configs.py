@@ -3,6 +3,7 @@ checked against the oracle on every output of every head (config 2 also
 through the exact path bench.py times); configs 4 and 5 on sampled rows the
 oracle computes one by one (all heads for config 4, one head of every KV
 group and more for config 5), plus properties that hold at any size."""
+import dataclasses
 import math
 
 import numpy as np
@@ -79,18 +80,15 @@ def test_config2_full_and_segment_sweep():
             assert_close(got, base, "bf16", f"c2 S={S} split={split} vs S=1024")
 
 
-def test_config2_timed_path_every_head():
-    """The exact path bench.py times: the 10k prompt through the library's
-    host scheduler, the descriptor inline in the prepare launch's arguments,
-    slots derived from the block table, the automatic (folded) plan; every
-    output of every head against the oracle run chunk by chunk with its own
-    scheduler, and every cache bit."""
-    need_gpu()
+def _timed_path_every_head(w, what):
+    """Run the prompt of workload w through bench.PromptBench (the path the
+    bench times) and check every output of every head against the oracle
+    run chunk by chunk with its own scheduler, and every cache bit.
+    Returns the per-chunk plan counts."""
     import bench
-    w = get_workload("c2")
-    pb = bench.PromptBench(1024, 0, workload="c2")
+    pb = bench.PromptBench(1024, 0, workload=w)
     assert pb.inline
-    say("config 2 through the timed path")
+    say(what)
     pb.step()
     torch.cuda.synchronize()
     got = pb.out.to(torch.float64).cpu().numpy()
@@ -112,13 +110,38 @@ def test_config2_timed_path_every_head():
                                 ob["cu_seqlens_q"], ob["cached_seq_len"], w.block_size)
         ref = oa.attention(q64[pos:pos + n], kp, vp, ob["block_table"], ob["cu_seqlens_q"],
                            ob["cached_seq_len"], w.block_size, w.scale, w.num_kv_heads)
-        assert_close(got[pos:pos + n], ref, "bf16", f"c2 timed path chunk at {pos}")
+        assert_close(got[pos:pos + n], ref, "bf16", f"{what}: chunk at {pos}")
         orc.commit()
         pos += n
     gk = pb.k_cache.view(torch.int16).permute(0, 2, 1, 3).contiguous().cpu().numpy()
     gv = pb.v_cache.view(torch.int16).permute(0, 3, 1, 2).contiguous().cpu().numpy()
     assert np.array_equal(gk, bits_of(kp, "bf16"))
     assert np.array_equal(gv, bits_of(vp, "bf16"))
+    return pb.plan
+
+
+def test_config2_timed_path_every_head():
+    """The exact path bench.py times: the 10k prompt through the library's
+    host scheduler, the descriptor inline in the prepare launch's arguments,
+    slots derived from the block table, the automatic plan (no key split at
+    this size); every output of every head against the oracle, and every
+    cache bit."""
+    need_gpu()
+    plan = _timed_path_every_head(get_workload("c2"), "config 2 through the timed path")
+    assert all(p["num_merge_rows"] == 0 for p in plan)
+
+
+def test_config2_tensor_parallel_share_every_head():
+    """One GPU's share of the 10k prompt under an eight-way split by KV-head
+    group ("Prefill Processing", section "Kernel Interface", tp_q): H 4 /
+    G 1, the bench's c2tp mode.  Each chunk's 64 row tiles leave most of the
+    GPU idle, so the automatic plan splits the prefill rows into key ranges
+    and merges their partial states; every output against the oracle."""
+    need_gpu()
+    w = get_workload("c2")
+    w = dataclasses.replace(w, num_heads=w.num_heads // w.num_kv_heads, num_kv_heads=1)
+    plan = _timed_path_every_head(w, "config 2 at one tensor-parallel share")
+    assert all(p["num_merge_rows"] > 0 for p in plan)
 
 
 def test_config3_prefix_shared_blocks():

@@ -1410,27 +1410,45 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
         mo += sp.merge;
     }
     __syncthreads();
-    // items and merge rows, one wave per sequence at a time (lanes over the
-    // sequence's items)
+    // Items and merge rows.  A sequence with few of them (a decode row: one
+    // per key range) is written by one thread, all such sequences at once; a
+    // longer one by one wave, lanes over its entries.  (One wave per
+    // sequence for all of them made a batch of 256 decodes spend ~20 us
+    // here.)
     const int wv = tid >> 6, ln = tid & 63;
     constexpr int kWaves = kThreads / 64;
-    // (issued sequences own contiguous item ranges: prefill ones, then decode ones)
-    for (int k = wv; k < B; k += kWaves) {        // k-th issued sequence
+    constexpr int kFew = 32;
+    auto write_items = [&](int k, int first, int step) {   // k-th issued sequence
         const int bq = s_seq[k];
         const int i0 = s_item[k], ni = s_item[k + 1] - i0;
         const int nsplit = s_nsplit[k];
         const int tiles = ni / nsplit;
         const int F = min(tiles, kPairSlots);
-        for (int local = ln; local < ni; local += 64) {
+        for (int local = first; local < ni; local += step) {
             const int li = local / nsplit;
             int rt = tiles - 1 - li;                     // longest row tiles first
             if (li < F && li >= F - F / 2) rt = tiles - F + (li - (F - F / 2));
             p.items[i0 + local] = make_int4(bq, rt, local % nsplit, nsplit);
         }
+    };
+    // (issued sequences own contiguous item ranges: prefill ones, then decode ones)
+    for (int k = tid; k < B; k += kThreads) {
+        if (s_item[k + 1] - s_item[k] <= kFew) write_items(k, 0, 1);
+    }
+    for (int k = wv; k < B; k += kWaves) {
+        if (s_item[k + 1] - s_item[k] > kFew) write_items(k, ln, 64);
+    }
+    for (int b = tid; b < B; b += kThreads) {
+        const int m0 = s_merge[b], m1 = s_merge[b + 1];
+        if (m1 - m0 <= kFew) {
+            for (int i = m0; i < m1; ++i) p.merge[i] = make_int2(b, i - m0);
+        }
     }
     for (int b = wv; b < B; b += kWaves) {
         const int m0 = s_merge[b], m1 = s_merge[b + 1];
-        for (int i = m0 + ln; i < m1; i += 64) p.merge[i] = make_int2(b, i - m0);
+        if (m1 - m0 > kFew) {
+            for (int i = m0 + ln; i < m1; i += 64) p.merge[i] = make_int2(b, i - m0);
+        }
     }
 }
 

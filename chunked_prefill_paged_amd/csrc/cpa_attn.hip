@@ -826,9 +826,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
             if (nfull > 1) btn = load_bt(tstart(1));
         }
         wait_vmem();                     // Q and the first block ids
-        // One tile.  The loop below calls it twice per iteration with buf a
-        // constant, so every LDS fragment read is a fixed register plus an
-        // immediate offset, with no address arithmetic in the tile.
+        // One tile.  With blocks of 64 keys or more the loop below calls it
+        // twice per iteration with buf a constant, so every LDS fragment read
+        // is a fixed register plus an immediate offset, with no address
+        // arithmetic in the tile.
         auto tile = [&](const int u, const int buf) __attribute__((always_inline)) {
             const int ts = tstart(u);
             if (!FP8 && u >= nfull) {    // the sequence's last tile

@@ -63,6 +63,9 @@ constexpr int kXcds = 8;
 // dispatcher hands an XCD's first such workgroups out across its CUs, CU j
 // taking the j-th and the (j + 32)-th.
 constexpr int kPairSlots = 64;
+// Prefill items that a mixed batch's plan keeps together when it spreads
+// them among the decode items.
+constexpr long long kPrefillRun = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // ---------------------------------------------------------------------------
@@ -1334,15 +1337,25 @@ __device__ PlanCounts block_scan_incl(PlanCounts x, PlanCounts* wtot) {
 
 // Work plan.  Items of prefill sequences (n > decode threshold) come first,
 // in sequence order, each sequence's longest row tiles first; items of
-// decode rows follow.  Long causal items thus start before the short ones,
-// and in a mixed batch the matrix-bound prefill items run while the
-// bandwidth-bound decode items fill the remaining slots.  Within the first
-// kPairSlots row tiles of a sequence (the F longest), the lighter half runs
-// in ascending order, so that a CU's two first workgroups are the j-th
-// longest and the j-th shortest of them: the causal triangle's long and
-// short rows share a CU, and the long one has the CU to itself once the
-// short one ends.
-__device__ void build_plan(const PrepParams& p, char* smem) {
+// decode rows follow.  Long causal items thus start before the short ones.
+// Within the first kPairSlots row tiles of a sequence (the F longest), the
+// lighter half runs in ascending order, so that a CU's two first workgroups
+// are the j-th longest and the j-th shortest of them: the causal triangle's
+// long and short rows share a CU, and the long one has the CU to itself
+// once the short one ends.
+//
+// With a bf16 cache and both kinds present (a mixed batch), the prefill
+// items are spread over the first three quarters of the decode items
+// instead (interleave), in runs of kPrefillRun consecutive items: taken all
+// at once they hold most of an XCD's slots and the decode items, whose rate
+// follows the slots they get, wait; spread, a prefill item shares its CU
+// with decode workgroups, which use the matrix cores little.  A run's items
+// (neighbouring row tiles) start together and read the same K/V tiles at
+// about the same time, so L2 serves their re-reads; single items spread
+// apart each fetched the sequence's K/V from HBM.  An fp8 cache keeps the
+// prefill items first: its decode workgroups convert codes with vector
+// instructions and slow a prefill workgroup beside them.
+__device__ void build_plan(const PrepParams& p, char* smem, bool interleave) {
     int* s_item = (int*)smem;                 // [kMaxSeqs + 1] first item of the k-th issued sequence
     int* s_merge = s_item + (kMaxSeqs + 1);   // [kMaxSeqs + 1] first merge row of sequence b
     int* s_nsplit = s_merge + (kMaxSeqs + 1); // [kMaxSeqs]     splits of the k-th issued sequence
@@ -1419,6 +1432,19 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
     const int wv = tid >> 6, ln = tid & 63;
     constexpr int kWaves = kThreads / 64;
     constexpr int kFew = 32;
+    // Position of the item issued i-th.  With interleave, prefill run m
+    // (items m * kPrefillRun ..) goes right before decode item
+    // floor(m * W / runs), W being three quarters of the decode items;
+    // decode item j then has the runs m with m * W < (j + 1) * runs, and
+    // their items, before it.
+    const long long W = interleave ? (items_all - items_pre) * 3 / 4 : 0;
+    const long long runs = (items_pre + kPrefillRun - 1) / kPrefillRun;
+    auto place = [&](long long i) -> long long {
+        if (items_pre == 0 || W == 0) return i;
+        if (i < items_pre) return i + ((i / kPrefillRun) * W) / runs;
+        const long long j = i - items_pre;
+        return j + min(items_pre, kPrefillRun * min(runs, ((j + 1) * runs + W - 1) / W));
+    };
     auto write_items = [&](int k, int first, int step) {   // k-th issued sequence
         const int bq = s_seq[k];
         const int i0 = s_item[k], ni = s_item[k + 1] - i0;
@@ -1429,7 +1455,7 @@ __device__ void build_plan(const PrepParams& p, char* smem) {
             const int li = local / nsplit;
             int rt = tiles - 1 - li;                     // longest row tiles first
             if (li < F && li >= F - F / 2) rt = tiles - F + (li - (F - F / 2));
-            p.items[i0 + local] = make_int4(bq, rt, local % nsplit, nsplit);
+            p.items[place(i0 + local)] = make_int4(bq, rt, local % nsplit, nsplit);
         }
     };
     // (issued sequences own contiguous item ranges: prefill ones, then decode ones)
@@ -1468,7 +1494,7 @@ __device__ void prep_body(const PrepParams& p, char* smem) {
             return;
         }
     }
-    build_plan(p, smem);
+    build_plan(p, smem, !FP8);
 }
 
 template <typename T, int D, bool ROPE, bool FP8>

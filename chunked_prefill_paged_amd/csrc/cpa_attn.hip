@@ -652,7 +652,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
     // a logit error of about 2^-9 * scale * |q| |k| that peaked softmaxes
     // (large logits) turn into output errors beyond the bf16 tolerance.
     f32x16 S0 = {}, S1 = {};
-    auto compute_tile = [&](int buf, int ts, bool masked) {
+    auto compute_tile = [&](int buf, int ts, bool masked) __attribute__((always_inline)) {
         if constexpr (kHandOrdered) {
             typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
             const char* kb = (const char*)&lds_k[buf][0];
@@ -816,69 +816,197 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
         auto load_bt8 = [&](int ts) -> int {
             return bt[min((ts >> lbs) + min(lane, nbt - 1), last_col)];
         };
-        if constexpr (FP8) {
-            load_tile_fp8(tstart(0), load_bt8(tstart(0)));
-            store_tile_fp8(0);
-            if (ntiles > 1) btn = load_bt8(tstart(1));
-        } else {
-            if (nfull > 0) {
-                const int bt0 = load_bt(tstart(0));
-                dma_k(tstart(0), 0, bt0);
-                dma_v(tstart(0), 0, bt0);
-            }
-            if (nfull > 1) btn = load_bt(tstart(1));
-        }
-        wait_vmem();                     // Q and the first block ids
-        // One tile.  With blocks of 64 keys or more the loop below calls it
-        // twice per iteration with buf a constant, so every LDS fragment read
-        // is a fixed register plus an immediate offset, with no address
-        // arithmetic in the tile.
-        auto tile = [&](const int u, const int buf) __attribute__((always_inline)) {
-            const int ts = tstart(u);
-            if (!FP8 && u >= nfull) {    // the sequence's last tile
-                load_tile_edge(ts);
-                store_tile(buf);
-            }
-            // this tile's gathers have landed (each wave waits for its own,
-            // the barrier for everyone's); all waves are done with buf ^ 1
-            wait_vmem();
-            __syncthreads();
+        // Decode items over an fp8 cache (all rows in wave 0: n * hpg <=
+        // 32) are bound by the tile bytes in flight: with every wave loading
+        // codes for the next tile and converting them after this one, one
+        // 16 KiB tile is in flight.  For them waves 1 and 2 stream the codes
+        // two tiles ahead through registers instead, converting and storing
+        // tile u + 1 into the other buffer after the barrier of tile u while
+        // wave 0 computes tile u; wave 3 only keeps the barriers.  (The same
+        // for a bf16 cache was not faster: its gathers straight into LDS
+        // already keep the decode rows at the rate HBM gives them.)
+        const bool stream8 = FP8 && kHandOrdered && rows_total <= 32 && ntiles >= 2;
+        if (stream8 && wave == 3) {
+            for (int u = 0; u < ntiles; ++u) __syncthreads();
+        } else if (stream8 && wave > 0) {
             if constexpr (FP8) {
-                if (u + 1 < ntiles) load_tile_fp8(tstart(u + 1), btn);
-                if (u + 2 < ntiles) btn = load_bt8(tstart(u + 2));
+                // A tile's K and V^T codes form 2 * NG groups of 64 16-byte
+                // chunks; loader wave w (1, 2) holds groups w - 1 + 2 i in its
+                // slot i, lane L chunk L of each: slots below NG / 2 hold K,
+                // the others V^T.  Every slot is one load on every path, so the
+                // compiler's wait counts stay exact across the loop.  A K group
+                // is KG consecutive keys of one block (block_size >= 16), 1 KiB
+                // contiguous from a wave-uniform base; a V^T group is DG rows d,
+                // lane L reading the 16 keys at chunk L % NC8V of row L / NC8V,
+                // whose block does not depend on the slot.
+                const uint8_t* k8 = (const uint8_t*)p.k_cache;
+                const uint8_t* v8 = (const uint8_t*)p.v_cache;
+                const int w1 = wave - 1;
+                constexpr int NG = kKeys * NC8K / 64;
+                constexpr int KG = 64 / NC8K, DG = 64 / NC8V;
+                constexpr int NSL = NG;                       // slots per loader lane (2 * NG groups, 2 waves)
+                static_assert(kKeys * NC8K == D * NC8V && NG * 64 == kKeys * NC8K && KG <= 16 && NG % 2 == 0,
+                              "whole groups; a K group inside the smallest block");
+                const int v_lane_key = (lane % NC8V) * 16;    // first key of this lane's V^T chunk
+                const int v_lane_off = (lane / NC8V) * bs + (v_lane_key & (bs - 1));
+                const int v_sel = v_lane_key >> lbs;          // its table entry, relative to the tile
+                auto v_base = [&](int ts, int btv) -> const uint8_t* {
+                    const uint32_t blk = min((uint32_t)__shfl(btv, v_sel), nb_max);
+                    return v8 + ((size_t)blk * G + g) * D * bs + (ts & (bs - 1)) + v_lane_off;
+                };
+                auto load_slot = [&](int ts, int btv, const uint8_t* vb, int i) -> u32x4 {
+                    if (i < NG / 2) {
+                        const int key0 = (w1 + 2 * i) * KG;
+                        const uint32_t blk = min((uint32_t)__builtin_amdgcn_readlane(btv, key0 >> lbs), nb_max);
+                        const uint8_t* kb = k8 + (((size_t)blk * G + g) * bs + (ts & (bs - 1)) + (key0 & (bs - 1))) * D;
+                        return *(const u32x4*)(kb + lane * 16);
+                    }
+                    return *(const u32x4*)(vb + (w1 + 2 * (i - NG / 2)) * DG * bs);
+                };
+                // slot i into LDS buffer buf as bf16, in store_tile_fp8's layout;
+                // the keys of a sequence's last tile past its end are zeroed
+                auto store_slot = [&](int buf, int ts, int i, u32x4 val) {
+                    const bool tail = ts + kKeys > kv_len;
+                    if (i < NG / 2) {
+                        const int key = (w1 + 2 * i) * KG + lane / NC8K, c8 = lane % NC8K;
+                        if (tail && ts + key >= kv_len) val = u32x4{0u, 0u, 0u, 0u};
+                        const int sw = swap_bits23(key & 31) & SWK;
+                        u32x4 lo, hi;
+                        fp8_to_bf16(val, lo, hi);
+                        *(u32x4*)&lds_k[buf][key * D + ((2 * c8) ^ sw) * EPC] = lo;
+                        *(u32x4*)&lds_k[buf][key * D + ((2 * c8 + 1) ^ sw) * EPC] = hi;
+                    } else {
+                        const int d = (w1 + 2 * (i - NG / 2)) * DG + lane / NC8V, kc = lane % NC8V;
+                        if (tail) {
+                            const int j = ts + v_lane_key;
+#pragma unroll
+                            for (int w = 0; w < 4; ++w) {
+                                const int keep = min(max(kv_len - j - 4 * w, 0), 4);
+                                val[w] &= keep >= 4 ? 0xffffffffu : ((1u << (8 * keep)) - 1u);
+                            }
+                        }
+                        const int sw = ((d & 7) ^ ((d >> 3) & 1)) & SWV;
+                        u32x4 lo, hi;
+                        fp8_to_bf16(val, lo, hi);
+                        *(u32x4*)&lds_v[buf][d * kKeys + ((2 * kc) ^ sw) * EPC] = lo;
+                        *(u32x4*)&lds_v[buf][d * kKeys + ((2 * kc + 1) ^ sw) * EPC] = hi;
+                    }
+                };
+                auto load_tile = [&](u32x4 (&st)[NSL], int u, int btv) __attribute__((always_inline)) {
+                    const int ts = tstart(u);
+                    const uint8_t* vb = v_base(ts, btv);
+#pragma unroll
+                    for (int i = 0; i < NSL; ++i) st[i] = load_slot(ts, btv, vb, i);
+                };
+                auto store_stage = [&](const u32x4 (&st)[NSL], int buf, int u) __attribute__((always_inline)) {
+                    const int ts = tstart(u);
+#pragma unroll
+                    for (int i = 0; i < NSL; ++i) store_slot(buf, ts, i, st[i]);
+                };
+                u32x4 st0[NSL], st1[NSL];
+                load_tile(st0, 0, load_bt8(tstart(0)));
+                load_tile(st1, 1, load_bt8(tstart(1)));
+                int btc = load_bt8(tstart(min(2, ntiles - 1)));       // ids of tile 2
+                store_stage(st0, 0, 0);
+                load_tile(st0, min(2, ntiles - 1), btc);
+                btc = load_bt8(tstart(min(3, ntiles - 1)));           // ids of tile 3
+                // Before the barrier of tile u: tile u is in buffer u & 1, tile
+                // u + 1 in stage (u + 1) & 1, tile u + 2 in stage u & 1, btc the
+                // ids of tile u + 3.  Tile indices past the item's last tile
+                // load the last tile again (from L2): every stage load is then
+                // unconditional, and the scheduling fences keep the ids' load
+                // ahead of the stage's, so the compiler waits for just the
+                // stage being stored and leaves the other one in flight.
+                for (int u = 0; u < ntiles; u += 2) {
+                    __syncthreads();                 // tile u stored; tile u - 1 computed
+                    if (u + 1 < ntiles) {
+                        const int btd = load_bt8(tstart(min(u + 4, ntiles - 1)));
+                        __builtin_amdgcn_sched_barrier(0);
+                        store_stage(st1, 1, u + 1);
+                        load_tile(st1, min(u + 3, ntiles - 1), btc);
+                        __builtin_amdgcn_sched_barrier(0);
+                        btc = btd;
+                        __syncthreads();             // tile u + 1 stored; tile u computed
+                        if (u + 2 < ntiles) {
+                            const int bte = load_bt8(tstart(min(u + 5, ntiles - 1)));
+                            __builtin_amdgcn_sched_barrier(0);
+                            store_stage(st0, 0, u + 2);
+                            load_tile(st0, min(u + 4, ntiles - 1), btc);
+                            __builtin_amdgcn_sched_barrier(0);
+                            btc = bte;
+                        }
+                    }
+                }
+            }
+        } else {
+            if constexpr (FP8) {
+                if (!stream8) {
+                    load_tile_fp8(tstart(0), load_bt8(tstart(0)));
+                    store_tile_fp8(0);
+                    if (ntiles > 1) btn = load_bt8(tstart(1));
+                }
             } else {
-                if (u + 1 < nfull) {
-                    dma_k(tstart(u + 1), buf ^ 1, btn);
-                    dma_v(tstart(u + 1), buf ^ 1, btn);
+                if (nfull > 0) {
+                    const int bt0 = load_bt(tstart(0));
+                    dma_k(tstart(0), 0, bt0);
+                    dma_v(tstart(0), 0, bt0);
                 }
-                if (u + 2 < nfull) btn = load_bt(tstart(u + 2));
+                if (nfull > 1) btn = load_bt(tstart(1));
             }
-            if (active(ts)) {
-                const bool masked = (ts + kKeys - 1 > c + wt_min) || (ts + kKeys > k1);
-                if constexpr (kHandOrdered) {
-                    compute_tile(buf, ts, masked);
+            wait_vmem();                     // Q and the first block ids
+            // One tile.  With blocks of 64 keys or more the loop below calls it
+            // twice per iteration with buf a constant, so every LDS fragment read
+            // is a fixed register plus an immediate offset, with no address
+            // arithmetic in the tile.
+            auto tile = [&](const int u, const int buf) __attribute__((always_inline)) {
+                const int ts = tstart(u);
+                if (!FP8 && u >= nfull) {    // the sequence's last tile
+                    load_tile_edge(ts);
+                    store_tile(buf);
+                }
+                // this tile's gathers have landed (each wave waits for its own,
+                // the barrier for everyone's); all waves are done with buf ^ 1
+                wait_vmem();
+                __syncthreads();
+                if constexpr (FP8) {
+                    if (!stream8) {
+                        if (u + 1 < ntiles) load_tile_fp8(tstart(u + 1), btn);
+                        if (u + 2 < ntiles) btn = load_bt8(tstart(u + 2));
+                    }
                 } else {
-                    qk(buf, S);
-                    update_ref(mask_max(ts, S));
-                    probs(S, pf);
-                    pv(buf, pf);
+                    if (u + 1 < nfull) {
+                        dma_k(tstart(u + 1), buf ^ 1, btn);
+                        dma_v(tstart(u + 1), buf ^ 1, btn);
+                    }
+                    if (u + 2 < nfull) btn = load_bt(tstart(u + 2));
                 }
+                if (active(ts)) {
+                    const bool masked = (ts + kKeys - 1 > c + wt_min) || (ts + kKeys > k1);
+                    if constexpr (kHandOrdered) {
+                        compute_tile(buf, ts, masked);
+                    } else {
+                        qk(buf, S);
+                        update_ref(mask_max(ts, S));
+                        probs(S, pf);
+                        pv(buf, pf);
+                    }
+                }
+                // the next tile of an fp8 cache goes into the other buffer, which
+                // every wave finished reading before this tile's barrier
+                if constexpr (FP8) {
+                    if (!stream8 && u + 1 < ntiles) store_tile_fp8(buf ^ 1);
+                }
+            };
+            if (bs >= kKeys) {
+                for (int u = 0; u < ntiles; u += 2) {
+                    tile(u, 0);
+                    if (u + 1 < ntiles) tile(u + 1, 1);
+                }
+            } else {
+                // (small blocks: one tile body, the buffer chosen at run time;
+                // two bodies measured slower here)
+                for (int u = 0; u < ntiles; ++u) tile(u, u & 1);
             }
-            // the next tile of an fp8 cache goes into the other buffer, which
-            // every wave finished reading before this tile's barrier
-            if constexpr (FP8) {
-                if (u + 1 < ntiles) store_tile_fp8(buf ^ 1);
-            }
-        };
-        if (bs >= kKeys) {
-            for (int u = 0; u < ntiles; u += 2) {
-                tile(u, 0);
-                if (u + 1 < ntiles) tile(u + 1, 1);
-            }
-        } else {
-            // (small blocks: one tile body, the buffer chosen at run time;
-            // two bodies measured slower here)
-            for (int u = 0; u < ntiles; ++u) tile(u, u & 1);
         }
     }
 

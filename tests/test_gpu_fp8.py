@@ -26,6 +26,15 @@ CASES = [
     ("mixed_decodes", 32, 8, 128, 16, 512, [(1300, 1024)], [1, 15, 16, 17, 600, 1111, 2049], 8192,
      0.05, 0.02),
     ("saturating", 8, 2, 128, 16, 512, [(400, 200)], [33], 4096, 0.004, 0.006),
+    # items whose rows all sit in the first wave (n * H/G <= 32) stream their
+    # tiles through two loader waves: decodes over larger blocks, short
+    # chunks with cached context (causal rows), one query head per KV head
+    ("rows_in_one_wave_bs64", 32, 8, 128, 64, 1024, [(308, 300), (5, 0), (132, 129)],
+     [64, 65, 127, 128, 129, 700, 2047, 3000], 8192, 0.05, 0.02),
+    ("rows_in_one_wave_bs256", 16, 4, 128, 256, 1024, [(1006, 1000)], [100, 255, 256, 257, 1500],
+     8192, 0.05, 0.02),
+    ("rows_in_one_wave_hpg1", 8, 8, 128, 32, 512, [(132, 100), (20, 0), (95, 64)], [77, 191], 8192,
+     0.05, 0.02),
 ]
 SPLITS = {"auto": (0, 0), "never": (-1, -1), "seg": ("S", "S")}
 

@@ -1329,24 +1329,37 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
             }
         }
     }
-    for (int cidx = tid; cidx < ntok * NCK; cidx += kThreads) {
-        const int tk = cidx / NCK, ch = cidx - (cidx / NCK) * NCK;
-        const size_t src = ((size_t)(tok0 + tk) * G + g) * D + ch * EPC;
-        const u32x4 vv = *(const u32x4*)(vn + src);
+    // all loads first (each thread's chunks of V, and of K unless rotated
+    // above), then the LDS and cache stores: one round trip per workgroup
+    constexpr int NIT = kCacheTok * NCK / kThreads;
+    static_assert(NIT * kThreads == kCacheTok * NCK, "chunks split evenly over the threads");
+    u32x4 vv[NIT], kv[NIT];
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+        const int cidx = tid + i * kThreads;
+        const int tk = cidx / NCK, ch = cidx - tk * NCK;
+        const size_t src = ((size_t)(tok0 + min(tk, ntok - 1)) * G + g) * D + ch * EPC;
+        vv[i] = *(const u32x4*)(vn + src);
+        if constexpr (!ROPE) kv[i] = *(const u32x4*)(kn + src);
+    }
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+        const int cidx = tid + i * kThreads;
+        const int tk = cidx / NCK, ch = cidx - tk * NCK;
+        if (tk >= ntok) continue;
         uint32_t* dst = (uint32_t*)(tile + tk * LD + ch * EPC);
-        dst[0] = vv.x;
-        dst[1] = vv.y;
-        dst[2] = vv.z;
-        dst[3] = vv.w;
+        dst[0] = vv[i].x;
+        dst[1] = vv[i].y;
+        dst[2] = vv[i].z;
+        dst[3] = vv[i].w;
         if constexpr (FP8) {
             // 8 bf16 of K -> 8 codes at the slot's row (D bytes)
-            const u32x4 kv = *(const u32x4*)(kn + src);
             const int64_t slot = s_slot[tk];
             if (slot >= 0 && slot < nslots) {
                 const int64_t blk = slot >> p.log2_bs;
                 const int off = (int)(slot & (bs - 1));
                 T e[8];
-                __builtin_memcpy(e, &kv, 16);
+                __builtin_memcpy(e, &kv[i], 16);
                 uint2 q8;
                 q8.x = fp8_pack4((float)e[0] * p.inv_k, (float)e[1] * p.inv_k, (float)e[2] * p.inv_k,
                                  (float)e[3] * p.inv_k);
@@ -1355,12 +1368,11 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
                 *(uint2*)((uint8_t*)p.k_cache + ((blk * G + g) * bs + off) * D + ch * 8) = q8;
             }
         } else if constexpr (!ROPE) {
-            const u32x4 kv = *(const u32x4*)(kn + src);
             const int64_t slot = s_slot[tk];
             if (slot >= 0 && slot < nslots) {
                 const int64_t blk = slot >> p.log2_bs;
                 const int off = (int)(slot & (bs - 1));
-                *(u32x4*)(kc + ((blk * G + g) * bs + off) * D + ch * EPC) = kv;
+                *(u32x4*)(kc + ((blk * G + g) * bs + off) * D + ch * EPC) = kv[i];
             }
         }
     }

@@ -1205,18 +1205,17 @@ __device__ inline float2 rope_cos_sin(int pos, double freq) {
     return make_float2(cn, sn);
 }
 
-// Rotation of one unit of a row: pairs ch*EPC .. ch*EPC + EPC - 1; cs(i)
-// gives cos/sin of pair i.
+// Rotation of one unit of a row: pairs ch*EPC .. ch*EPC + EPC - 1, whose
+// two source chunks ua, ub come from rope_load; cs(i) gives cos/sin of pair
+// i.  The rotated chunks go to the same places of the row at dst.
 template <typename T, int D, typename CS>
-__device__ inline void rope_rows(const T* src, T* dst, int ch, CS cs, bool interleaved) {
+__device__ inline void rope_rotate_store(u32x4 ua, u32x4 ub, T* dst, int ch, CS cs, bool interleaved) {
     constexpr int EPC = 16 / sizeof(T);
     constexpr int NCK = D / EPC;
     // unit ch covers pairs ch*EPC .. ch*EPC + EPC - 1 of the row: chunks ch
     // and ch + NCK/2 (rotate-half) or chunks 2ch and 2ch + 1 (interleaved)
     const int ca = interleaved ? 2 * ch : ch;
     const int cb = interleaved ? 2 * ch + 1 : ch + NCK / 2;
-    u32x4 ua = *(const u32x4*)(src + ca * EPC);
-    u32x4 ub = *(const u32x4*)(src + cb * EPC);
     T va[EPC], vb[EPC];
     __builtin_memcpy(va, &ua, 16);
     __builtin_memcpy(vb, &ub, 16);
@@ -1245,6 +1244,16 @@ __device__ inline void rope_rows(const T* src, T* dst, int ch, CS cs, bool inter
     *(u32x4*)(dst + ca * EPC) = ua;
     *(u32x4*)(dst + cb * EPC) = ub;
 }
+
+// The two source chunks of a rotation unit (see rope_rotate_store).
+template <typename T, int D>
+__device__ inline void rope_load(const T* src, int ch, bool interleaved, u32x4& ua, u32x4& ub) {
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr int NCK = D / EPC;
+    ua = *(const u32x4*)(src + (interleaved ? 2 * ch : ch) * EPC);
+    ub = *(const u32x4*)(src + (interleaved ? 2 * ch + 1 : ch + NCK / 2) * EPC);
+}
+
 
 // Absolute position of token tok: its sequence b by binary search over
 // cu_seqlens_q, then cached_seq_len[b] + (tok - cu[b]).  *seq receives b.
@@ -1289,6 +1298,34 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
     T* vc = (T*)p.v_cache;
     const int bs = p.block_size;
     const int64_t nslots = (int64_t)p.num_blocks * bs;
+    // this thread's chunks of V, and of K unless rotated, loaded before
+    // anything else (they depend on no slot): the LDS and cache stores come
+    // after the slots, one round trip per workgroup
+    constexpr int NIT = kCacheTok * NCK / kThreads;
+    static_assert(NIT * kThreads == kCacheTok * NCK, "chunks split evenly over the threads");
+    u32x4 vv[NIT], kv[NIT];
+#pragma unroll
+    for (int i = 0; i < NIT; ++i) {
+        const int cidx = tid + i * kThreads;
+        const int tk = cidx / NCK, ch = cidx - tk * NCK;
+        const size_t src = ((size_t)(tok0 + min(tk, ntok - 1)) * G + g) * D + ch * EPC;
+        vv[i] = *(const u32x4*)(vn + src);
+        if constexpr (!ROPE) kv[i] = *(const u32x4*)(kn + src);
+    }
+    // (with RoPE: the two source chunks of each of this thread's K rotation
+    // units, rotated once the positions are known)
+    constexpr int NKU = ROPE ? kCacheTok * (NCK / 2) / kThreads : 1;   // rotation units per thread
+    static_assert(!ROPE || NKU * kThreads == kCacheTok * (NCK / 2), "units split evenly over the threads");
+    u32x4 ka[NKU], kb[NKU];
+    if constexpr (ROPE) {
+        const bool inter = p.rope == 2;
+#pragma unroll
+        for (int i = 0; i < NKU; ++i) {
+            const int u = tid + i * kThreads;
+            const int tk = u / (NCK / 2), ch = u - tk * (NCK / 2);
+            rope_load<T, D>(kn + ((size_t)(tok0 + min(tk, ntok - 1)) * G + g) * D, ch, inter, ka[i], kb[i]);
+        }
+    }
     // slots of the tokens: given, or derived from the block table at the
     // token's position
     __shared__ int64_t s_slot[kCacheTok];
@@ -1316,31 +1353,20 @@ __device__ void cache_write(const PrepParams& p, char* smem) {
         // keys: rotate, then store at the slot (one KV head per workgroup,
         // so each (token, pair) angle is used once: no table)
         const bool inter = p.rope == 2;
-        for (int u = tid; u < ntok * (NCK / 2); u += kThreads) {
+#pragma unroll
+        for (int i = 0; i < NKU; ++i) {
+            const int u = tid + i * kThreads;
             const int tk = u / (NCK / 2), ch = u - tk * (NCK / 2);
+            if (tk >= ntok) continue;
             const int64_t slot = s_slot[tk];
             if (slot >= 0 && slot < nslots) {
                 const int64_t blk = slot >> p.log2_bs;
                 const int off = (int)(slot & (bs - 1));
                 const int pos = s_pos[tk];
-                rope_rows<T, D>(kn + ((size_t)(tok0 + tk) * G + g) * D,
-                                kc + ((blk * G + g) * bs + off) * D, ch,
-                                [&](int i) { return rope_cos_sin(pos, s_freq[i]); }, inter);
+                rope_rotate_store<T, D>(ka[i], kb[i], kc + ((blk * G + g) * bs + off) * D, ch,
+                                        [&](int i) { return rope_cos_sin(pos, s_freq[i]); }, inter);
             }
         }
-    }
-    // all loads first (each thread's chunks of V, and of K unless rotated
-    // above), then the LDS and cache stores: one round trip per workgroup
-    constexpr int NIT = kCacheTok * NCK / kThreads;
-    static_assert(NIT * kThreads == kCacheTok * NCK, "chunks split evenly over the threads");
-    u32x4 vv[NIT], kv[NIT];
-#pragma unroll
-    for (int i = 0; i < NIT; ++i) {
-        const int cidx = tid + i * kThreads;
-        const int tk = cidx / NCK, ch = cidx - tk * NCK;
-        const size_t src = ((size_t)(tok0 + min(tk, ntok - 1)) * G + g) * D + ch * EPC;
-        vv[i] = *(const u32x4*)(vn + src);
-        if constexpr (!ROPE) kv[i] = *(const u32x4*)(kn + src);
     }
 #pragma unroll
     for (int i = 0; i < NIT; ++i) {
@@ -1428,12 +1454,27 @@ __device__ void rope_queries(const PrepParams& p, int qgrp) {
     const int H = p.num_heads;
     const T* qs = (const T*)p.q;
     T* qd = (T*)p.q_out;
-    for (int u = tid; u < ntok * H * (NCK / 2); u += kThreads) {
-        const int row = u / (NCK / 2), ch = u - row * (NCK / 2);
-        const int tk = row / H;
-        const size_t r = ((size_t)tok0 * H + row) * D;
-        const float2* cs = s_cs + tk * (D / 2);
-        rope_rows<T, D>(qs + r, qd + r, ch, [&](int i) { return cs[i]; }, inter);
+    // kQB units per thread at a time, their loads first
+    constexpr int kQB = 4;
+    const int nunits = ntok * H * (NCK / 2);
+    for (int u0 = tid; u0 < nunits; u0 += kQB * kThreads) {
+        u32x4 qa[kQB], qb[kQB];
+#pragma unroll
+        for (int k = 0; k < kQB; ++k) {
+            const int u = min(u0 + k * kThreads, nunits - 1);
+            const int row = u / (NCK / 2), ch = u - row * (NCK / 2);
+            rope_load<T, D>(qs + ((size_t)tok0 * H + row) * D, ch, inter, qa[k], qb[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kQB; ++k) {
+            const int u = u0 + k * kThreads;
+            if (u >= nunits) break;
+            const int row = u / (NCK / 2), ch = u - row * (NCK / 2);
+            const int tk = row / H;
+            const float2* cs = s_cs + tk * (D / 2);
+            rope_rotate_store<T, D>(qa[k], qb[k], qd + ((size_t)tok0 * H + row) * D, ch,
+                                    [&](int i) { return cs[i]; }, inter);
+        }
     }
 }
 

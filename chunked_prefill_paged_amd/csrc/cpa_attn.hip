@@ -403,6 +403,42 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
         if constexpr (FP8) {
             const uint8_t* k8 = (const uint8_t*)p.k_cache;
             const uint8_t* v8 = (const uint8_t*)p.v_cache;
+            if (ts + kKeys <= kv_len) {
+                // A full tile: no guards.  The 8 keys of a wave's K chunks of
+                // one slot lie in one block (block_size >= 16), so its id is
+                // wave-uniform and the block base scalar; a thread's offsets
+                // within the blocks do not change from tile to tile.
+                const size_t blk8 = (size_t)G * bs * D;        // bytes of one block
+                const uint32_t tsb = ts & (bs - 1);             // the tile's start within its block
+                // (the thread's offsets are formed here, per tile, in 32 bits
+                // from an unsigned thread index: kept across the loop they
+                // would cost registers the tile needs)
+                uint32_t t = tid;
+                asm volatile("" : "+v"(t));
+#pragma unroll
+                for (int i = 0; i < NL8; ++i) {
+                    const uint32_t cidx = i * kThreads + t;
+                    const uint32_t key = cidx / NC8K, c8 = cidx % NC8K;
+                    const int key0 = (i * kThreads + wave * 64) / NC8K;
+                    const uint32_t blk = min((uint32_t)__builtin_amdgcn_readlane(btv, key0 >> lbs), nb_max);
+                    const uint8_t* kb = k8 + blk * blk8 + ((size_t)g * bs + tsb) * D;   // wave-uniform
+                    f8k[i] = *(const u32x4*)(kb + ((key & (bs - 1)) * D + c8 * 16));
+                }
+#pragma unroll
+                for (int i = 0; i < NL8; ++i) {
+                    const uint32_t cidx = i * kThreads + t;
+                    const uint32_t d = cidx / NC8V, kc = cidx % NC8V;
+                    const uint32_t off = (g * D + d) * bs + tsb + ((kc * 16) & (bs - 1));
+                    if (bs >= kKeys) {
+                        const uint32_t blk = min((uint32_t)__builtin_amdgcn_readlane(btv, 0), nb_max);
+                        f8v[i] = *(const u32x4*)(v8 + blk * blk8 + off);
+                    } else {
+                        const uint32_t blk = min((uint32_t)__shfl(btv, (kc * 16) >> lbs), nb_max);
+                        f8v[i] = *(const u32x4*)(v8 + blk * blk8 + off);
+                    }
+                }
+                return;
+            }
 #pragma unroll
             for (int i = 0; i < NL8; ++i) {
                 const int cidx = i * kThreads + tid;

@@ -28,15 +28,22 @@
 //     8 consecutive keys; with V stored transposed in the cache
 //     ([block, head, D, block_size]) the PV A operand is then a plain 16-byte
 //     LDS read.  O^T = V^T P^T accumulates in 4 (D=128) 32x32 fp32 tiles.
-//   * K and V^T tiles of 64 keys are gathered through the block table with
-//     16-byte loads into registers, double-buffered in LDS (XOR-swizzled
-//     16-byte chunks against bank conflicts), one barrier per tile.
+//   * K and V^T tiles of 64 keys are gathered through the block table and
+//     double-buffered in LDS (XOR-swizzled 16-byte chunks against bank
+//     conflicts), one barrier per tile.  A bf16 cache's full tiles go
+//     straight into LDS (global_load_lds_dwordx4); an fp8 cache's codes go
+//     through registers and become bf16 on the way into LDS; decode items
+//     over an fp8 cache stream their codes two tiles ahead through two
+//     loader waves.
 //   * Masking is a select to -inf before exp2; keys at or past the
-//     sequence's end are never loaded (zero-filled), so stale or NaN slots
-//     cannot reach the MFMA.
+//     sequence's end reach LDS as zeros (not loaded, or loaded from the
+//     sequence's last block and zeroed), so stale or NaN slots cannot reach
+//     the MFMA.
 //   * Workgroup ids are remapped so that each of the 8 XCDs runs a
 //     contiguous range of (KV head, item) pairs: one KV head per XCD L2 when
-//     G = 8.  Items are ordered longest-first within a sequence.
+//     G = 8.  Items are ordered longest-first within a sequence; a mixed
+//     batch over a bf16 cache spreads its prefill items among the decode
+//     items.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>

@@ -15,7 +15,13 @@ pairs = n*c + n(n+1)/2 ("Prefill Optimisation ...", section 4), over the
 wall time of the steps -> TFLOP/s, and as a fraction of the MI355X dense
 bf16 MFMA peak.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--clock-warmup-s S] [--no-cpu-baseline]
+
+Before the W warmup steps the headline mode runs untimed steps for S seconds
+(default 0.25; the count is in the line's "clock_warmup"): an idle GPU's
+shader clock ramps up over ~0.1 s of continuous work, so after a few warmup
+steps alone the timed steps would measure the ramp.  --clock-warmup-s 0
+gives the cold-clock number.
     python bench.py --copy-probe      # one plain 1 GiB device copy, for
                                       # calibrating HBM byte counters
 
@@ -66,6 +72,10 @@ def _args():
                          "in one varlen call; c5: the 32k prompt, per chunk and against one "
                          "monolithic call; c4: the mixed decode + prefill batch; rope: the cache "
                          "write with rotary embedding fused in, at two chunk shapes")
+    ap.add_argument("--clock-warmup-s", type=float, default=0.25,
+                    help="seconds of untimed steps before the warmup steps (the 10k-prompt modes): "
+                         "an idle GPU's shader clock ramps up over ~0.1 s of continuous work "
+                         "(0: none)")
     ap.add_argument("--steady-warmup", type=int, default=100,
                     help="after the timed steps, this many more untimed steps, then the same "
                          "number of timed steps again: the steady-state rate (0: skip)")
@@ -645,6 +655,29 @@ def _steps(torch, bench, n):
         ra.after()
 
 
+def _clock_warmup(torch, bench, seconds):
+    """Untimed steps until `seconds` of wall time have passed, the GPU kept
+    busy throughout: the shader clock of an idle MI355X measures ~2.18 GHz
+    and climbs to ~2.43 GHz over the first ~0.1 s of continuous work, so a
+    short warmup would time the climb.  Returns (steps, seconds)."""
+    if seconds <= 0:
+        return 0, 0.0
+    ra = RunAhead(torch)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        ra.before()
+        bench.step()
+        ra.after()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                break
+    torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
+
+
 def _timed_steps(torch, args, bench):
     """K timed steps with the per-launch attention events; returns (wall
     seconds, attention ms summed over launches, mean ms per chunk)."""
@@ -695,6 +728,7 @@ def run_prompt(args):
     gc.collect()
     gc.freeze()
     gc.disable()
+    cw_steps, cw_s = _clock_warmup(torch, bench, args.clock_warmup_s)
     _steps(torch, bench, args.warmup)
     torch.cuda.synchronize()
     elapsed, attn_ms, per_chunk_ms = _timed_steps(torch, args, bench)
@@ -734,6 +768,9 @@ def run_prompt(args):
                                 if args.event_timing == "dispatch" else
                                 "HIP event records around every attention call of the timed steps")},
         "plan": [{"items": p["num_items"], "merge_rows": p["num_merge_rows"]} for p in bench.plan],
+        "clock_warmup": {"steps": cw_steps, "seconds": round(cw_s, 3),
+                         "why": "untimed steps before the warmup steps: an idle GPU's shader "
+                                "clock ramps up over ~0.1 s of continuous work"},
     }
     if args.steady_warmup > 0:
         # the same measurement again after more untimed steps: the first
@@ -742,7 +779,7 @@ def run_prompt(args):
         torch.cuda.synchronize()
         el2, attn2, chunks2 = _timed_steps(torch, args, bench)
         line["steady_state"] = {
-            "untimed_steps_before": args.warmup + args.steps + args.steady_warmup,
+            "untimed_steps_before": cw_steps + args.warmup + args.steps + args.steady_warmup,
             "value": round(flops * args.steps / el2 / 1e12, 2),
             "ms_per_step": round(el2 * 1e3 / args.steps, 4),
             "roofline_achieved": round(flops * args.steps / (attn2 / 1e3) / 1e12, 2),

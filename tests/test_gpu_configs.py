@@ -244,6 +244,15 @@ def test_config4_mixed_batch_sampled():
     out, _ = gpu_call(cache, pb, qt, kt, vt, w.kv_segment_size)
     got = out.to(torch.float64).numpy()
     assert np.isfinite(got).all()
+    # every decode row, all heads, bit for bit against the decodes alone: the
+    # mixed plan places the prefill items among the decode items, and each
+    # decode item must still run exactly once with the same partials
+    dec = {"cu_seqlens_q": np.ascontiguousarray(pb["cu_seqlens_q"][:257]),
+           "cached_seq_len": np.ascontiguousarray(pb["cached_seq_len"][:256]),
+           "block_table": np.ascontiguousarray(pb["block_table"][:256]),
+           "slot_mapping": np.ascontiguousarray(pb["slot_mapping"][:256])}
+    out_dec, _ = gpu_call(cache, dec, qt[:256], kt[:256], vt[:256], w.kv_segment_size)
+    assert torch.equal(out_dec, out[:256]), "decode rows differ between the mixed and the decode-only plan"
     # the step's writes, bit for bit, at the oracle's slots
     kb = cache.k.view(torch.int16)
     vb = cache.v.view(torch.int16)

@@ -33,7 +33,7 @@
 //     conflicts), one barrier per tile.  A bf16 cache's full tiles go
 //     straight into LDS (global_load_lds_dwordx4); an fp8 cache's codes go
 //     through registers and become bf16 on the way into LDS; decode items
-//     over an fp8 cache stream their codes two tiles ahead through two
+//     over an fp8 cache stream their codes three tiles ahead through two
 //     loader waves.
 //   * Masking is a select to -inf before exp2; keys at or past the
 //     sequence's end reach LDS as zeros (not loaded, or loaded from the
@@ -863,7 +863,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
         // 32) are bound by the tile bytes in flight: with every wave loading
         // codes for the next tile and converting them after this one, one
         // 16 KiB tile is in flight.  For them waves 1 and 2 stream the codes
-        // two tiles ahead through registers instead, converting and storing
+        // three tiles ahead through registers instead, converting and storing
         // tile u + 1 into the other buffer after the barrier of tile u while
         // wave 0 computes tile u; wave 3 only keeps the barriers.  (The same
         // for a bf16 cache was not faster: its gathers straight into LDS
@@ -946,38 +946,55 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnParams p) {
 #pragma unroll
                     for (int i = 0; i < NSL; ++i) store_slot(buf, ts, i, st[i]);
                 };
-                u32x4 st0[NSL], st1[NSL];
-                load_tile(st0, 0, load_bt8(tstart(0)));
-                load_tile(st1, 1, load_bt8(tstart(1)));
-                int btc = load_bt8(tstart(min(2, ntiles - 1)));       // ids of tile 2
-                store_stage(st0, 0, 0);
-                load_tile(st0, min(2, ntiles - 1), btc);
-                btc = load_bt8(tstart(min(3, ntiles - 1)));           // ids of tile 3
-                // Before the barrier of tile u: tile u is in buffer u & 1, tile
-                // u + 1 in stage (u + 1) & 1, tile u + 2 in stage u & 1, btc the
-                // ids of tile u + 3.  Tile indices past the item's last tile
-                // load the last tile again (from L2): every stage load is then
-                // unconditional, and the scheduling fences keep the ids' load
-                // ahead of the stage's, so the compiler waits for just the
-                // stage being stored and leaves the other one in flight.
-                for (int u = 0; u < ntiles; u += 2) {
+                u32x4 sa[NSL], sb[NSL], sc[NSL];
+                auto last = [&](int u) { return min(u, ntiles - 1); };
+                // (the prologue issues its last loads in the loop's order:
+                // a stage, its ids register, the next stage, ... so the
+                // wait counts the compiler carries into the loop are the
+                // loop's own)
+                const int id0 = load_bt8(tstart(0)), id1 = load_bt8(tstart(1));
+                const int id2 = load_bt8(tstart(last(2))), id3 = load_bt8(tstart(last(3)));
+                load_tile(sa, 0, id0);
+                load_tile(sb, 1, id1);
+                int ida = load_bt8(tstart(last(4)));
+                load_tile(sc, last(2), id2);
+                int idb = load_bt8(tstart(last(5)));
+                store_stage(sa, 0, 0);
+                load_tile(sa, last(3), id3);
+                int idc = load_bt8(tstart(last(6)));
+                // Before the barrier of tile u (u a multiple of 3): tile u is
+                // in buffer u & 1, tiles u + 1, u + 2, u + 3 in sb, sc, sa,
+                // and ida, idb, idc hold the ids of tiles u + 4, u + 5, u + 6.
+                // Each step stores one stage, reloads it three tiles ahead
+                // and then reloads its ids register three tiles ahead: no
+                // register changes hands, every load is issued on every path
+                // (tiles past the item's last repeat it, from L2), so the
+                // wait before a store drains just that stage and leaves the
+                // other two in flight.  (The steady loop has no branch; the
+                // last one to three tiles follow it.)
+                auto step = [&](u32x4 (&st)[NSL], int& id, int t) __attribute__((always_inline)) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    store_stage(st, t & 1, t);
+                    load_tile(st, last(t + 3), id);
+                    id = load_bt8(tstart(last(t + 6)));
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                int u = 0;
+                for (; u + 3 < ntiles; u += 3) {
                     __syncthreads();                 // tile u stored; tile u - 1 computed
-                    if (u + 1 < ntiles) {
-                        const int btd = load_bt8(tstart(min(u + 4, ntiles - 1)));
-                        __builtin_amdgcn_sched_barrier(0);
-                        store_stage(st1, 1, u + 1);
-                        load_tile(st1, min(u + 3, ntiles - 1), btc);
-                        __builtin_amdgcn_sched_barrier(0);
-                        btc = btd;
-                        __syncthreads();             // tile u + 1 stored; tile u computed
-                        if (u + 2 < ntiles) {
-                            const int bte = load_bt8(tstart(min(u + 5, ntiles - 1)));
-                            __builtin_amdgcn_sched_barrier(0);
-                            store_stage(st0, 0, u + 2);
-                            load_tile(st0, min(u + 4, ntiles - 1), btc);
-                            __builtin_amdgcn_sched_barrier(0);
-                            btc = bte;
-                        }
+                    step(sb, ida, u + 1);
+                    __syncthreads();
+                    step(sc, idb, u + 2);
+                    __syncthreads();
+                    step(sa, idc, u + 3);
+                }
+                __syncthreads();
+                if (u + 1 < ntiles) {
+                    step(sb, ida, u + 1);
+                    __syncthreads();
+                    if (u + 2 < ntiles) {
+                        step(sc, idb, u + 2);
+                        __syncthreads();
                     }
                 }
             }

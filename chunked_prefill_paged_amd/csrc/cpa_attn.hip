@@ -1974,7 +1974,7 @@ cpa_status launch_prep(const cpa_attn_args* a, const Resolved* r, bool plan, con
     const int grid = p.cache_wgs + p.rope_wgs + (plan ? 1 : 0);
     if (grid == 0) return CPA_OK;
     if constexpr (FP8) {
-        if (rope) return CPA_ERR_UNSUPPORTED;
+        if (rope) return CPA_ERR_UNSUPPORTED;   // (refused earlier by check_rope)
     }
     if (inline_desc(a)) {
         // the host copies go into the launch's own arguments
@@ -2108,6 +2108,7 @@ cpa_status check_rope(const cpa_attn_args* a, const cpa_rope_args* rope) {
     if (a->total_q > 0 && (!a->q || !rope->q_out || a->num_seqs <= 0 ||
                            (!inline_desc(a) && (!a->cu_seqlens_q || !a->cached_seq_len))))
         return CPA_ERR_INVALID_ARG;
+    if (kv_fp8(a)) return CPA_ERR_UNSUPPORTED;   // the rotating cache write stores bf16 rows
     return CPA_OK;
 }
 

@@ -254,7 +254,9 @@ typedef struct cpa_rope_args {
  * num_heads, num_seqs, cu_seqlens_q and cached_seq_len (positions are
  * needed even when slot_mapping is given).  CPA_ERR_INVALID_ARG for a NULL
  * rope, a bad theta or interleaved flag, num_heads not a multiple of
- * num_kv_heads, or a missing pointer. */
+ * num_kv_heads, or a missing pointer; CPA_ERR_UNSUPPORTED with an FP8
+ * cache (kv_dtype CPA_FP8_E4M3): the rotation is written into bf16 rows
+ * only. */
 cpa_status cpa_rope_reshape_and_cache(const cpa_attn_args* args, const cpa_rope_args* rope,
                                       void* stream);
 

@@ -194,6 +194,16 @@ def test_bad_rope_requests_are_refused(rope, over):
     assert _lib.lib().cpa_rope_chunked_prefill_attn(ctypes.byref(a), p, None) == _lib.CPA_ERR_INVALID_ARG
 
 
+def test_rope_with_an_fp8_cache_is_unsupported():
+    # the rotating cache write stores bf16 rows only
+    a, _keep = _args()
+    a.kv_dtype = 2                                # CPA_FP8_E4M3
+    p = ctypes.byref(_rope())
+    assert _lib.lib().cpa_rope_reshape_and_cache(ctypes.byref(a), p, None) == _lib.CPA_ERR_UNSUPPORTED
+    assert _lib.lib().cpa_rope_prepare(ctypes.byref(a), p, None) == _lib.CPA_ERR_UNSUPPORTED
+    assert _lib.lib().cpa_rope_chunked_prefill_attn(ctypes.byref(a), p, None) == _lib.CPA_ERR_UNSUPPORTED
+
+
 def test_binding_struct_matches_the_header(tmp_path):
     """Size and field offsets of cpa_attn_args as the C compiler lays it out
     against the binding's ctypes mirror, and the inline-descriptor limit."""

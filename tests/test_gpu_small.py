@@ -7,6 +7,7 @@ import pytest
 import torch
 
 from chunked_prefill_paged_amd import AttnCall
+from oracle import attention as oa
 
 from tests.gpu_helpers import (DEV, Pair, assert_close, bits_of, gpu_call, need_gpu, quantize,
                                say)
@@ -294,3 +295,47 @@ def test_empty_sequence_in_batch_and_lse():
         got = out.to(torch.float64).numpy()
         for h in range(H):
             assert np.abs(got[:, h] - want[:, h // (H // G)]).max() <= 2e-2
+
+
+def test_largest_batch_in_one_call():
+    """The largest batch one call takes (4096 sequences): 4095 decodes over
+    contexts of 1..700 keys (one or two key segments each, so many rows
+    merge) and one 1700-token chunk at cached 300, whose prefill items the
+    plan spreads in runs among the decode items; every output element
+    against the oracle."""
+    need_gpu()
+    H, G, D, bs, S, dtype = 8, 2, 64, 16, 512, "bf16"
+    rng = np.random.default_rng(4096)
+    ctx = rng.integers(1, 701, size=4095)
+    prompt, computed = 2000, 300
+    lens = [int(c) for c in ctx] + [computed]
+    max_blocks = -(-(prompt + 1) // bs) + 1
+    nb = sum(-(-(L + 1) // bs) for L in ctx) + -(-prompt // bs) + 41
+    pair = Pair(nb, G, bs, D, dtype, 8192, max_blocks, rng.permutation(nb).astype(np.int32))
+    for i, c in enumerate(ctx):
+        pair.add_decode(i, int(c))
+    pair.add_partial(4095, prompt, computed)
+    # every sequence's context in one cache-write call, and once into the
+    # oracle's pools
+    tot = sum(lens)
+    kt, k64 = quantize(rng.standard_normal((tot, G, D)), dtype)
+    vt, v64 = quantize(rng.standard_normal((tot, G, D)), dtype)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    slots = np.concatenate([pair.prod.slots(r, 0, L) for r, L in enumerate(lens)])
+    batch = {"cu_seqlens_q": cu, "cached_seq_len": np.zeros(len(lens), np.int32),
+             "block_table": np.zeros((len(lens), 1), np.int32), "slot_mapping": slots}
+    gpu_call(pair.cache, batch, None, kt, vt, 0, only_cache=True)
+    blocks = [pair.orc._find(r).blocks for r in range(len(lens))]
+    pair.k_pool, pair.v_pool = oa.cache_write(pair.k_pool, pair.v_pool, k64, v64, blocks, cu,
+                                              np.zeros(len(lens), np.int32), bs)
+    pb, ob = pair.step()
+    assert pb["num_seqs"] == 4096
+    T = pb["num_tokens"]
+    qt, q64 = quantize(rng.standard_normal((T, H, D)), dtype)
+    kt, k64 = quantize(rng.standard_normal((T, G, D)), dtype)
+    vt, v64 = quantize(rng.standard_normal((T, G, D)), dtype)
+    say(f"largest batch: {pb['num_seqs']} sequences, T={T}, pool {nb} blocks")
+    scale = 1 / math.sqrt(D)
+    out, _ = gpu_call(pair.cache, pb, qt, kt, vt, S, scale=scale)
+    ref = pair.oracle_batch(ob, q64, k64, v64, scale, G)
+    assert_close(out.to(torch.float64).numpy(), ref, dtype, "largest batch")
